@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""NVFP4-KV decode attention benchmark on one MI355X.
+
+One step = one decode layer-step of the hot path for the whole batch:
+  quantise-on-append of the n_q new K/V rows per sequence (into NVFP4),
+  split-K decode partial pass over the packed cache, combine pass.
+Throughput `value` is effective KV GB/s: packed KV bytes read per step / step time
+(inputs resident in HBM). The packed cache is rotated over enough copies (>= 1 GiB
+in all) that successive steps cannot be served from the 256 MB Infinity Cache.
+
+The K timed steps are captured into one HIP graph (the pages' engine decodes with
+exact-batch graphs: knoopx/ninfer page, "Capabilities and limits") and replayed
+once between events on the launch stream. Each kernel's average duration comes
+from a graph of K launches of that kernel alone, timed the same way.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4-KV decode attention µs/layer-step + effective KV GB/s (% HBM peak)"
+HBM_PEAK_GBS = 8000.0
+ROTATE_MIN_BYTES = 1 << 30
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "internal.h"):
+        h.update(open(os.path.join(ROOT, "quantized_kv_decode_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_partial_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """The fp64 oracle timed on the host on a bounded sample of the same workload:
+    repeated decode steps (quantise the n_q new rows, attention for every query row)
+    over the full cache until about budget_s seconds have elapsed."""
+    import numpy as np
+    import oracle
+    import workloads
+    nthreads = oracle.default_threads()
+    k = workloads.all_kv_rows(w, "k")
+    v = workloads.all_kv_rows(w, "v")
+    ku, vu = workloads.as_u16(k), workloads.as_u16(v)
+    g = oracle.calibrate(ku, vu, w.seq_lens)
+    cache = oracle.Cache(w.num_kv_heads, w.head_dim, w.capacity)
+    oracle.append(cache, ku, vu, g, w.seq_base, [0] * w.batch, list(w.seq_lens), nthreads)
+    q = workloads.as_u16(workloads.queries(w))
+    rows = [r for b in range(w.batch) for r in range(w.seq_base[b] + w.seq_lens[b] - w.n_q,
+                                                     w.seq_base[b] + w.seq_lens[b])]
+    kn, vn = np.ascontiguousarray(ku[rows]), np.ascontiguousarray(vu[rows])
+    wp = [L - w.n_q for L in w.seq_lens]
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.append(cache, kn, vn, g, w.seq_base, wp, [w.n_q] * w.batch, nthreads)
+        oracle.attention(cache, g, q, w.seq_base, w.seq_lens, w.n_q, w.sm_scale, nthreads=nthreads)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 1000:
+            break
+    return {"value": round(w.kv_bytes * steps / el / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{steps} full decode step(s) of {w.name} (append n_q rows + fp64 attention for all "
+                      f"{w.batch * w.n_q * w.num_q_heads} query rows over the whole cache), {el:.1f} s",
+            "ms_per_step": round(el / steps * 1e3, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_27b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import quantized_kv_decode_amd as qk
+    import workloads
+
+    qk.load_library()
+    w = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+
+    # ---- resident inputs: one calibrated, filled pool, then rotation copies
+    log(f"workload {w.name}: {w.description}")
+    pool0 = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev)
+    g = torch.empty((w.batch, w.num_kv_heads, 2), dtype=torch.float32, device=dev)
+    kdev, vdev = [], []
+    for b in range(w.batch):                                   # upload per sequence
+        kdev.append(workloads.kv_rows(w, "k", b).to(dev))
+        vdev.append(workloads.kv_rows(w, "v", b).to(dev))
+    kall, vall = torch.cat(kdev), torch.cat(vdev)
+    del kdev, vdev
+    qk.calibrate(pool0, kall, vall, list(w.seq_lens), out=g)
+    if w.append_rows:                                          # prefill chunk appended on its own
+        L0 = w.capacity - w.append_rows
+        qk.append(pool0, kall[:L0].contiguous(), vall[:L0].contiguous(), g, [0], [0], [L0])
+    else:
+        qk.append(pool0, kall, vall, g, w.seq_base, [0] * w.batch, list(w.seq_lens))
+    rows = torch.cat([torch.arange(w.seq_base[b] + w.seq_lens[b] - w.n_q, w.seq_base[b] + w.seq_lens[b])
+                      for b in range(w.batch)]).to(dev)
+    k_step, v_step = kall[rows].contiguous(), vall[rows].contiguous()
+    chunk = None
+    if w.append_rows:
+        chunk = (kall[w.capacity - w.append_rows:].contiguous(), vall[w.capacity - w.append_rows:].contiguous())
+    del kall, vall
+    q = workloads.queries(w).to(dev)
+    if chunk is not None:
+        qk.append(pool0, chunk[0], chunk[1], g, [0], [w.capacity - w.append_rows], [w.append_rows])
+    R = max(1, math.ceil(ROTATE_MIN_BYTES / pool0.nbytes)) if pool0.nbytes < (256 << 20) * 2 else 1
+    pools = [pool0] + [qk.KVPool.from_planes(pool0.k_codes.clone(), pool0.k_scales.clone(), pool0.v_codes.clone(),
+                                             pool0.v_scales.clone()) for _ in range(R - 1)]
+    ws = qk.alloc_workspace(pool0, list(w.seq_lens), w.n_q, w.num_q_heads, dev)
+    out = torch.empty((w.batch, w.n_q, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"cache {pool0.nbytes / 1e6:.1f} MB x {R} rotation copies; workspace {ws.numel() / 1e6:.2f} MB")
+
+    wp = [L - w.n_q for L in w.seq_lens]
+    nq = [w.n_q] * w.batch
+    seq_lens = list(w.seq_lens)
+
+    def k_append(p):
+        qk.append(p, k_step, v_step, g, w.seq_base, wp, nq)
+
+    def k_partial(p):
+        qk.decode_attn_partial(p, g, q, w.seq_base, seq_lens, w.sm_scale, ws)
+
+    def k_combine(p):
+        qk.decode_attn_combine(p, g, out, seq_lens, ws)
+
+    def step(i):
+        p = pools[i % R]
+        k_append(p)
+        k_partial(p)
+        k_combine(p)
+
+    # ---- warmup (eager) and the reference output of the eager path
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    def capture(fn_list, n):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(n):
+                    for fn in fn_list:
+                        fn(pools[i % R])
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        return graph
+
+    def time_graph(graph, reps=1):
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        graph.replay()                                        # untimed replay: graph upload
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(s)
+        e1.synchronize()
+        return e0.elapsed_time(e1)                            # ms
+
+    g_step = capture([k_append, k_partial, k_combine], K)
+    g_part = capture([k_partial], K)
+    g_comb = capture([k_combine], K)
+    g_app = capture([k_append], K)
+
+    # ---- timed region: exactly K steps
+    torch.cuda.synchronize()
+    ms_total = time_graph(g_step)
+    ms_step = ms_total / K
+    ms_part = time_graph(g_part) / K
+    ms_comb = time_graph(g_comb) / K
+    ms_app = time_graph(g_app) / K
+    chunk_res = None
+    if chunk is not None:
+        # the prefill-chunk append of this workload, reported on its own
+        def k_chunk(p):
+            qk.append(p, chunk[0], chunk[1], g, [0], [w.capacity - w.append_rows], [w.append_rows])
+        ms_chunk = time_graph(capture([k_chunk], K)) / K
+        rd = w.append_rows * w.num_kv_heads * w.head_dim * 2 * 2
+        wr = w.append_rows * w.num_kv_heads * (w.head_dim // 2 + w.head_dim // 16) * 2
+        chunk_res = {"rows": w.append_rows, "us": round(ms_chunk * 1e3, 3), "bytes_read": rd, "bytes_written": wr,
+                     "GBps": round((rd + wr) / (ms_chunk * 1e-3) / 1e9, 2)}
+    out_graph = out.clone()
+    step(0)                                                    # eager step on copy 0: same result
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_graph), "graph replay and eager step disagree"
+
+    kv = w.kv_bytes
+    achieved = kv / (ms_part * 1e-3) / 1e9
+    traffic = read_traffic(w.name)
+    res = {
+        "metric": METRIC,
+        "value": round(kv / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 6),
+        "us_per_layer_step": round(ms_step * 1e3, 3),
+        "pct_hbm_peak": round(kv / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "seq_lens": list(w.seq_lens),
+            "num_kv_heads": w.num_kv_heads,
+            "num_q_heads": w.num_q_heads,
+            "head_dim": w.head_dim,
+            "n_q": w.n_q,
+            "kv_format": "nvfp4 (e2m1 codes + e4m3 group-16 scales + fp32 per-(seq, kv head) scale)",
+            "kv_bytes_per_step": kv,
+            "rotation_copies": R,
+            "timing": "one HIP-graph replay of K steps between events",
+            "step": "append n_q rows/seq + split-K partial + combine",
+        },
+        "kernels_us": {"append": round(ms_app * 1e3, 3), "decode_partial": round(ms_part * 1e3, 3),
+                       "decode_combine": round(ms_comb * 1e3, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_partial", "algorithmic_bytes_per_launch": kv},
+    }
+    if chunk_res is not None:
+        res["append_chunk"] = chunk_res
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,153 @@
+/*
+ * nvfp4_kv.h -- C ABI of the MI355X (gfx950) NVFP4-KV decode-attention library.
+ *
+ * The method (gzenz/ninfer page, section "Context and model", bullet "NVFP4 KV
+ * cache"): K and V rows are stored as 4-bit E2M1 codes with one E4M3 scale per
+ * group of 16 elements, "45% less KV VRAM than int8". The calls follow the
+ * pages' statement of the problem: a per-engine KV dtype, one startup-fixed KV
+ * pool shared by the active requests, each request with its own logical length
+ * (knoopx/ninfer page, "Capabilities and limits": one to eight active requests,
+ * "one shared startup-fixed KV pool", MTP draft windows of one to five, format
+ * and shape combinations served by explicitly implemented native paths, so
+ * unsupported ones are rejected, not emulated).
+ *
+ * ---------------------------------------------------------------- layout ----
+ * A pool holds, for each of num_kv_heads heads and capacity token slots:
+ *   k_codes, v_codes   uint8 [num_kv_heads][capacity][head_dim/2]
+ *                      byte j of a row = code(2j) | code(2j+1) << 4 (even element
+ *                      in the low nibble); a code is sign<<3 | E2M1 magnitude code.
+ *   k_scales, v_scales uint8 [num_kv_heads][capacity][head_dim/16]
+ *                      byte j = E4M3 (OCP E4M3FN) code of the scale of elements
+ *                      [16j, 16j+16); always in 0x00..0x7E (never negative/NaN).
+ *   global_scale       float [num_seqs][num_kv_heads][2], index 0 = K, 1 = V:
+ *                      g = fp32(amax / (6*448)) over that sequence's rows of that
+ *                      head (second-level scale; not on the pages, a stated reading).
+ * Element value: x_hat = e2m1(code) * e4m3(scale) * g.
+ * Sequence b owns slots [seq_base[b], seq_base[b] + length) in every head plane.
+ * Quantisation rounds the exact real ratios amax_group/(6g) and |x|/(S g) to the
+ * nearest E4M3 / E2M1 value, ties to the even code, saturating at 448 / 6; the
+ * input's sign bit becomes the code's sign bit; g == 0 gives scale 0 and zero
+ * magnitudes.
+ *
+ * ------------------------------------------------------------ conventions ---
+ * - Every device pointer is allocated and owned by the caller. The library never
+ *   allocates, frees or synchronises; each call validates its arguments on the
+ *   host, then only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *   default stream) and returns. Host arrays are read during the call only.
+ * - Device pointers must be 16-byte aligned. bf16 is IEEE bfloat16 bit patterns.
+ * - Functions are stateless and thread-safe; the last error message is
+ *   thread-local.
+ * - Return value: 0 on success, else one of the negative codes below, checked
+ *   before any launch (a failed call enqueues nothing), except NVFP4_EHIP which
+ *   reports a launch failure. NaN or infinite inputs in device memory are the
+ *   caller's responsibility (results are then unspecified).
+ */
+#ifndef NVFP4_KV_H
+#define NVFP4_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_OK            0
+#define NVFP4_EINVAL       (-1)  /* null or unaligned pointer, count out of range      */
+#define NVFP4_EUNSUPPORTED (-2)  /* shape with no native path (see each call)           */
+#define NVFP4_ERANGE       (-3)  /* slots past capacity, length shorter than n_q        */
+#define NVFP4_EWORKSPACE   (-4)  /* workspace smaller than the size query returned      */
+#define NVFP4_EHIP         (-5)  /* a kernel launch failed (message: nvfp4_last_error)  */
+
+#define NVFP4_OUT_F32  0
+#define NVFP4_OUT_BF16 1
+
+#define NVFP4_MAX_SEQS 8         /* active sequences per call                         */
+#define NVFP4_MAX_ROWS 64        /* GQA group x query tokens sharing one KV head      */
+
+/* The caller-owned pool. head_dim must be 128 or 256; num_kv_heads >= 1;
+ * capacity >= 1 token slots per head plane. */
+typedef struct nvfp4_kv_cache {
+    void   *k_codes;
+    void   *k_scales;
+    void   *v_codes;
+    void   *v_scales;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int64_t capacity;
+} nvfp4_kv_cache;
+
+/* Global scales from the rows that will be stored (second-level per-(sequence,
+ * KV head) scale; a stated reading, the pages do not give it).
+ *   k_rows, v_rows: device bf16 [sum(n_rows)][num_kv_heads][head_dim], the rows of
+ *                   sequence 0, then sequence 1, ...
+ *   n_rows:         host int64 [num_seqs], each >= 0 (0 gives g = 0)
+ *   global_scale:   device float [num_seqs][num_kv_heads][2], written:
+ *                   g[b][h][0|1] = fp32(max |x| over sequence b's K|V rows of head h / 2688)
+ * Errors: EINVAL (null/unaligned pointers, num_seqs < 1, n_rows < 0),
+ *         EUNSUPPORTED (num_seqs > 8, head_dim not 128/256). */
+int nvfp4_kv_calibrate(const nvfp4_kv_cache *cache, const void *k_rows, const void *v_rows,
+                       int32_t num_seqs, const int64_t *n_rows, float *global_scale,
+                       void *stream);
+
+/* Quantise-on-append: writes n_new[b] K and V rows of sequence b at slots
+ * seq_base[b] + write_pos[b] + r (r < n_new[b]) of every head plane. Lengths are
+ * the caller's to advance. Each 16-element group gets its E4M3 scale from its own
+ * maximum and the given g; rows whose values exceed 2688 g saturate.
+ *   k_new, v_new:  device bf16 [sum(n_new)][num_kv_heads][head_dim], concatenated over b
+ *   global_scale:  device float [num_seqs][num_kv_heads][2]
+ *   seq_base, write_pos, n_new: host int64 [num_seqs]; n_new[b] >= 0
+ * Errors: EINVAL, EUNSUPPORTED (num_seqs > 8, head_dim), ERANGE (a slot outside
+ *         [0, capacity)). Sequences must not write overlapping slots. */
+int nvfp4_kv_append(const nvfp4_kv_cache *cache, const void *k_new, const void *v_new,
+                    const float *global_scale, int32_t num_seqs, const int64_t *seq_base,
+                    const int64_t *write_pos, const int64_t *n_new, void *stream);
+
+/* Bytes of device workspace nvfp4_decode_attn (and its two halves below) need
+ * for these arguments; 0 if the arguments are invalid (the decode call then
+ * reports why). The split-K plan depends only on the arguments. */
+size_t nvfp4_decode_attn_workspace_bytes(const nvfp4_kv_cache *cache, int32_t num_seqs,
+                                         const int64_t *seq_len, int32_t n_q,
+                                         int32_t num_q_heads);
+
+/* Grouped-query decode attention read directly from the NVFP4 pool.
+ *   q:        device bf16 [num_seqs][n_q][num_q_heads][head_dim]
+ *   out:      device [num_seqs][n_q][num_q_heads][head_dim], fp32 or bf16 (out_dtype;
+ *             bf16 is the round-to-nearest-even of the fp32 result)
+ *   seq_len:  host int64 [num_seqs]; the length INCLUDES the n_q query tokens, whose
+ *             K/V rows were already appended. Query token i of sequence b sees keys
+ *             [0, seq_len[b] - n_q + i] (bottom-right causal among the n_q tokens).
+ *   seq_base: host int64 [num_seqs]
+ *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   out = softmax(sm_scale * q . k_hat) . v_hat, computed with fp32 accumulation.
+ * Errors: EINVAL (pointers, out_dtype, n_q < 1, non-finite sm_scale),
+ *         EUNSUPPORTED (head_dim, num_q_heads % num_kv_heads != 0, num_seqs > 8,
+ *         (num_q_heads/num_kv_heads) * n_q > 64), ERANGE (seq_len < n_q, slots past
+ *         capacity), EWORKSPACE (workspace_bytes below the size query). */
+int nvfp4_decode_attn(const nvfp4_kv_cache *cache, const float *global_scale, const void *q,
+                      void *out, int32_t out_dtype, int32_t num_seqs, const int64_t *seq_base,
+                      const int64_t *seq_len, int32_t n_q, int32_t num_q_heads, float sm_scale,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* The two kernels of nvfp4_decode_attn, callable on their own (same arguments,
+ * same workspace) so that each can be timed: the split-K partial pass writes
+ * per-split (o, m, l) into the workspace; the combine pass merges them by
+ * log-sum-exp, applies the V global scale and writes out. */
+int nvfp4_decode_attn_partial(const nvfp4_kv_cache *cache, const float *global_scale,
+                              const void *q, int32_t num_seqs, const int64_t *seq_base,
+                              const int64_t *seq_len, int32_t n_q, int32_t num_q_heads,
+                              float sm_scale, void *workspace, size_t workspace_bytes,
+                              void *stream);
+int nvfp4_decode_attn_combine(const nvfp4_kv_cache *cache, const float *global_scale,
+                              void *out, int32_t out_dtype, int32_t num_seqs,
+                              const int64_t *seq_len, int32_t n_q, int32_t num_q_heads,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Message describing the last failure on this thread ("" if none). */
+const char *nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_KV_H */

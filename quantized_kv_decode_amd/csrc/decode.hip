@@ -1,0 +1,585 @@
+// Split-K grouped-query decode attention over the NVFP4 KV pool (gfx950).
+//
+// What is computed (gzenz/ninfer page, "Context and model": attention reads K/V
+// stored as E2M1 codes + E4M3 group-16 scales; knoopx/ninfer page, "Capabilities
+// and limits": batched decode of 1-8 requests and MTP verification of 1 + 1..5
+// draft tokens): for every query row, softmax(sm_scale * q . k_hat) . v_hat over
+// the visible keys, with k_hat = e2m1 * S * g_K and v_hat = e2m1 * S * g_V.
+//
+// Work decomposition. A unit is (sequence b, KV head kh, token range); one
+// 256-thread workgroup runs one unit, its four waves taking alternate 32-token
+// blocks. Every query row that reads KV head kh -- GQA group G times n_q query
+// tokens, R <= 64 rows, padded to NT tiles of 16 -- shares each KV block, so a
+// block is loaded and dequantised once for all of them.
+//
+// Per 32-token block and wave (MFMA v_mfma_f32_16x16x32_f16, lane l = 16 g + n):
+//   S^T = K . Q^T   A = K (16 tokens x 32 d), B = Q^T (32 d x 16 rows), two token
+//                   tiles. Lane (g, n) loads token n's d-range [D/4 g, D/4 (g+1)):
+//                   D/8 contiguous code bytes + D/64 scale bytes. The contraction
+//                   index d is permuted identically in Q, so no transpose is needed.
+//                   Result lane (g, n): tokens 16 mt + 4 g + i, row 16 rt + n.
+//   softmax         fp32, base 2, per row (lane column n); cross-lane max over the
+//                   four lane groups only; the running reference m is raised
+//                   lazily (only when a score exceeds it by more than 2^8), so the
+//                   accumulator rescale is rare.
+//   O += P . V      A = P (16 rows x 32 tokens, straight from the S^T layout),
+//                   B = V (32 tokens x 16 d). The d index of output column n of
+//                   tile dt is EPL n + dt (EPL = D/16), so lane n's B values for
+//                   every tile lie in ONE 16-element scale group of each token:
+//                   8 (or 4) contiguous code bytes and one scale byte per token.
+//                   Codes of two tokens are interleaved nibble-wise (v_bfi) so one
+//                   fp4->fp16 convert yields a (token, token) k-pair.
+// Dequantisation: v_cvt_scalef32_pk_f16_fp4 (scale 1) gives exact E2M1 in fp16;
+// the E4M3 byte shifted left by 7 is the fp16 of S * 2^-8, and one v_pk_mul_f16
+// forms e2m1 * S * 2^-8 exactly (at most 6 significant bits, >= 2^-18). The 2^8
+// and g factors are folded into the score scale and the final output scale.
+// Q rows are converted to fp16 after an exact power-of-two scaling that brings
+// the row maximum to [2^14, 2^15).
+//
+// Each workgroup merges its four waves' (o, m, l) through LDS and writes one
+// partial per unit; the combine kernel merges the units of a (sequence, head)
+// by log-sum-exp in a fixed order (deterministic: no atomics).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "internal.h"
+
+namespace nvfp4 {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMax = 8.0f;      // raise the softmax reference only past m + 8 (base 2)
+
+__device__ inline half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ inline uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// fp16 pair (S * 2^-8, S * 2^-8) from an E4M3 byte 0x00..0x7E.
+__device__ inline uint32_t scale_pair(uint32_t byte) { return (byte << 7) | (byte << 23); }
+
+template <int SEL>
+__device__ inline uint32_t fp4x2(uint32_t w) {
+    return as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+}
+
+__device__ inline uint32_t hmul2(uint32_t a, uint32_t b) { return as_u32(as_h2(a) * as_h2(b)); }
+
+__device__ inline uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
+
+__device__ inline float wave_max_g(float x) {    // max over the four lane groups (lanes n, n+16, n+32, n+48)
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+
+template <int D>
+struct Raw {
+    static constexpr int EPL = D / 16;            // PV output tiles; d-values per token per lane
+    static constexpr int KW = D / 32;             // K code dwords per token per lane
+    static constexpr int VW = EPL / 8;            // V code dwords per token per lane
+    uint32_t k[2][KW];                            // two 16-token tiles
+    uint32_t ks[2];                               // K scale bytes (D/64 of them) per tile
+    uint32_t v[8][VW];                            // 8 tokens (k-slots) per lane
+    uint32_t vs[8];                               // V scale byte per token
+};
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over one head plane: loads past its end return zeros (no fault).
+__device__ inline rsrc_t plane_rsrc(const uint8_t *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Byte offsets of one lane's first load in each stream for the block starting at
+// slot `slot0` (= seq_base + block start); later tokens of the block are
+// immediate offsets. Tokens past the sequence end are read (finite values, or
+// zeros past the plane) and masked out of the softmax.
+struct Offs {
+    uint32_t kc, ks, vc, vs;
+};
+
+template <int D>
+__device__ inline Offs lane_offsets(int64_t slot0, int g, int n) {
+    constexpr int EPL = D / 16;
+    Offs o;
+    o.kc = (uint32_t)((slot0 + n) * (D / 2) + (D / 8) * g);
+    o.ks = (uint32_t)((slot0 + n) * (D / 16) + (D / 64) * g);
+    o.vc = (uint32_t)((slot0 + 4 * g) * (D / 2) + (EPL / 2) * n);
+    o.vs = (uint32_t)((slot0 + 4 * g) * (D / 16) + (EPL * n) / 16);
+    return o;
+}
+
+template <int D>
+__device__ inline void load_k(Raw<D> &r, rsrc_t kc, rsrc_t ks, const Offs &o) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const uint32_t oc = o.kc + 16 * mt * (D / 2);
+        const uint32_t os = o.ks + 16 * mt * (D / 16);
+        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, oc, 0, 0);
+        r.k[mt][0] = a[0]; r.k[mt][1] = a[1]; r.k[mt][2] = a[2]; r.k[mt][3] = a[3];
+        if constexpr (D == 256) {
+            const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(kc, oc + 16, 0, 0);
+            r.k[mt][4] = b[0]; r.k[mt][5] = b[1]; r.k[mt][6] = b[2]; r.k[mt][7] = b[3];
+            r.ks[mt] = __builtin_amdgcn_raw_buffer_load_b32(ks, os, 0, 0);
+        } else {
+            r.ks[mt] = __builtin_amdgcn_raw_buffer_load_b16(ks, os, 0, 0);
+        }
+    }
+}
+
+template <int D>
+__device__ inline void load_v(Raw<D> &r, rsrc_t vc, rsrc_t vs, const Offs &o) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t dtok = 16 * (j >> 2) + (j & 3);
+        if constexpr (D == 256) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(vc, o.vc + dtok * (D / 2), 0, 0);
+            r.v[j][0] = a[0]; r.v[j][1] = a[1];
+        } else {
+            r.v[j][0] = __builtin_amdgcn_raw_buffer_load_b32(vc, o.vc + dtok * (D / 2), 0, 0);
+        }
+        r.vs[j] = __builtin_amdgcn_raw_buffer_load_b8(vs, o.vs + dtok * (D / 16), 0, 0);
+    }
+}
+
+template <int D, int NT>
+struct State {
+    static constexpr int EPL = D / 16;
+    float4_t acc[NT][EPL];   // O rows 16 rt + 4 g + i, d = EPL n + dt
+    float4_t lsum[NT];       // row sums of the fp16 P actually multiplied into O (P . 1), same rows
+    float m[NT];             // running reference of row 16 rt + n (base 2)
+};
+
+template <int D>
+__device__ inline half8_t dequant_k(const Raw<D> &r, int mt, int kk) {
+    const uint32_t w = r.k[mt][kk];
+    const uint32_t sp = scale_pair((r.ks[mt] >> (8 * (kk >> 1))) & 0xFFu);
+    const u32x4_t a = {hmul2(fp4x2<0>(w), sp), hmul2(fp4x2<1>(w), sp), hmul2(fp4x2<2>(w), sp),
+                       hmul2(fp4x2<3>(w), sp)};
+    return __builtin_bit_cast(half8_t, a);
+}
+
+// S^T tiles for the block: s[mt][rt] lane (g, n) = scores of tokens 16 mt + 4 g + i, row 16 rt + n.
+template <int D, int NT>
+__device__ inline void qk_block(float4_t (&s)[2][NT], const Raw<D> &r, const half8_t *qlds, int lane) {
+    constexpr int KK = D / 32;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) s[mt][rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const half8_t a0 = dequant_k<D>(r, 0, kk);
+        const half8_t a1 = dequant_k<D>(r, 1, kk);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const half8_t qf = qlds[(rt * KK + kk) * 64 + lane];
+            s[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf, s[0][rt], 0, 0, 0);
+            s[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qf, s[1][rt], 0, 0, 0);
+        }
+    }
+}
+
+// V codes of token pairs (k-slots 2kp, 2kp+1) interleaved nibble-wise, and their scale pairs.
+template <int D>
+struct VPrep {
+    static constexpr int VW = D / 128;
+    uint32_t E[4][VW], O[4][VW], SP[4];
+};
+
+template <int D>
+__device__ inline void v_prep(VPrep<D> &vp, const Raw<D> &r) {
+    constexpr int VW = D / 128;
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+#pragma unroll
+        for (int h = 0; h < VW; ++h) {
+            const uint32_t wa = r.v[2 * kp][h], wb = r.v[2 * kp + 1][h];
+            vp.E[kp][h] = bfi(0x0F0F0F0Fu, wa, wb << 4);   // byte b: (A elem 2b, B elem 2b)
+            vp.O[kp][h] = bfi(0x0F0F0F0Fu, wa >> 4, wb);   // byte b: (A elem 2b+1, B elem 2b+1)
+        }
+        // bit 7 cleared: stored scales never have it; bytes read past a sequence's end
+        // (masked, p = 0) must stay finite so 0 * v stays 0.
+        vp.SP[kp] = ((r.vs[2 * kp] & 0x7Fu) << 7) | ((r.vs[2 * kp + 1] & 0x7Fu) << 23);
+    }
+}
+
+// Scores -> probabilities for one block. lim = L - n_q - tb: key at offset o of the
+// block is visible to query token i iff o <= lim + i (bottom-right causal; offsets
+// past the sequence end are never visible). Blocks with lim >= 31 need no mask.
+template <int D, int NT, bool MASK>
+__device__ inline void scores_block(float (&x)[NT][8], float (&mrow)[NT], const float4_t (&s)[2][NT],
+                                    const float (&cexp)[NT], const int (&qi)[NT], int lim, int g) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float v = s[j >> 2][rt][j & 3] * cexp[rt];
+            if constexpr (MASK) {
+                const int o = 16 * (j >> 2) + 4 * g + (j & 3);
+                if (o > lim + qi[rt]) v = -INFINITY;
+            }
+            x[rt][j] = v;
+            mloc = fmaxf(mloc, v);
+        }
+        mrow[rt] = wave_max_g(mloc);
+    }
+}
+
+template <int D, int NT>
+__device__ inline void softmax_block(State<D, NT> &st, const float4_t (&s)[2][NT], half8_t (&pa)[NT],
+                                     const float (&cexp)[NT], const int (&qi)[NT], int lim, int g) {
+    constexpr int EPL = D / 16;
+    float x[NT][8], mrow[NT];
+    if (lim >= kBlockTokens - 1)
+        scores_block<D, NT, false>(x, mrow, s, cexp, qi, lim, g);
+    else
+        scores_block<D, NT, true>(x, mrow, s, cexp, qi, lim, g);
+    bool need_any = false;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) need_any |= mrow[rt] > st.m[rt] + kLazyMax;
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {   // rare after the first block
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const bool need = mrow[rt] > st.m[rt] + kLazyMax;
+            const float mnew = need ? mrow[rt] : st.m[rt];
+            const float alpha = need ? exp2f(st.m[rt] - mnew) : 1.0f;   // m = -inf -> 0
+            st.m[rt] = mnew;
+            // accumulator rows 4 g + i live in lane column n' = 4 g + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * g + i);
+                st.lsum[rt][i] *= ai;
+#pragma unroll
+                for (int dt = 0; dt < EPL; ++dt) st.acc[rt][dt][i] *= ai;
+            }
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        const float mu = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = exp2f(x[rt][j] - mu);
+        pa[rt] = half8_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                         (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+    }
+}
+
+template <int D, int NT>
+__device__ inline void pv_block(State<D, NT> &st, const VPrep<D> &vp, const half8_t (&pa)[NT]) {
+    constexpr int EPL = D / 16;
+#pragma unroll
+    for (int dt = 0; dt < EPL; ++dt) {
+        const int h = dt >> 3, byte = (dt & 7) >> 1;
+        uint32_t bw[4];
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp) {
+            const uint32_t src = (dt & 1) ? vp.O[kp][h] : vp.E[kp][h];
+            uint32_t c;
+            switch (byte) {
+                case 0: c = fp4x2<0>(src); break;
+                case 1: c = fp4x2<1>(src); break;
+                case 2: c = fp4x2<2>(src); break;
+                default: c = fp4x2<3>(src); break;
+            }
+            bw[kp] = hmul2(c, vp.SP[kp]);
+        }
+        const half8_t bh = __builtin_bit_cast(half8_t, u32x4_t{bw[0], bw[1], bw[2], bw[3]});
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+            st.acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], bh, st.acc[rt][dt], 0, 0, 0);
+    }
+    // l from the same fp16 P through the matrix core: P . 1 (fp16 1.0 = 0x3C00)
+    const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+        st.lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], ones, st.lsum[rt], 0, 0, 0);
+}
+
+template <int D, int NT>
+struct Lds {
+    static constexpr int KK = D / 32;
+    static constexpr int STRIDE = D + 4;                       // merge rows, padded
+    static constexpr int Q_BYTES = NT * KK * 64 * 16;          // Q fragments [NT][KK][lane]
+    static constexpr int MERGE_BYTES = kWaves * 16 * STRIDE * 4;
+    static constexpr int BYTES = Q_BYTES > MERGE_BYTES ? Q_BYTES : MERGE_BYTES;
+};
+
+template <int D, int NT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+void decode_partial_kernel(DecodeParams p) {
+    constexpr int KK = D / 32;
+    constexpr int EPL = D / 16;
+    constexpr int QD = D / 4;
+    using LD = Lds<D, NT>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LD::BYTES];
+    __shared__ float sm_c[kMaxRows];
+    __shared__ float sm_m[kWaves][kMaxRows];
+    __shared__ float sm_l[kWaves][kMaxRows];
+
+    const int u = blockIdx.x;
+    int b = 0;
+#pragma unroll
+    for (int s = 1; s < kMaxSeqs; ++s)
+        if (s < p.B && u >= p.unit_base[s]) b = s;
+    const int local = u - p.unit_base[b];
+    const int kh = local / p.n_split[b];
+    const int sp = local - kh * p.n_split[b];
+    const int64_t L = p.seq_len[b];
+    const int64_t t0 = (int64_t)sp * p.split_len[b];
+    const int64_t t1 = min(t0 + (int64_t)p.split_len[b], L);
+    const int nblk = (int)((t1 - t0 + kBlockTokens - 1) / kBlockTokens);
+
+    // wave index is uniform across the wave; readfirstlane lets the compiler keep the
+    // block loop on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int R = p.R, G = p.G;
+    const int64_t base = p.seq_base[b];
+    const uint32_t code_bytes = (uint32_t)(p.cap * (D / 2)), scale_bytes = (uint32_t)(p.cap * (D / 16));
+    const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * code_bytes, code_bytes);
+    const rsrc_t ks = plane_rsrc(p.ks + (int64_t)kh * scale_bytes, scale_bytes);
+    const rsrc_t vc = plane_rsrc(p.vc + (int64_t)kh * code_bytes, code_bytes);
+    const rsrc_t vs = plane_rsrc(p.vs + (int64_t)kh * scale_bytes, scale_bytes);
+    half8_t *qlds = reinterpret_cast<half8_t *>(lds);
+
+    // ---- Q rows -> fp16 fragments in LDS (wave rt converts row tile rt):
+    // fragment (rt, kk, lane (g, n)) = row 16 rt + n, d in [QD g + 8 kk, QD g + 8 kk + 8)
+    if (wave < NT) {
+        const int rt = wave;
+        const int row = 16 * rt + n;
+        const bool valid = row < R;
+        uint32_t w[KK * 4];
+        if (valid) {
+            const int i = row / G;
+            const int h = kh * G + (row - i * G);
+            const uint16_t *qr = p.q + (((int64_t)b * p.n_q + i) * p.Hq + h) * D + QD * g;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(qr + 8 * kk);
+                w[4 * kk] = v.x; w[4 * kk + 1] = v.y; w[4 * kk + 2] = v.z; w[4 * kk + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KK * 4; ++k) w[k] = 0u;
+        }
+        uint32_t am = 0;
+#pragma unroll
+        for (int k = 0; k < KK * 4; ++k) am = max(am, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+        am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+        am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+        // exact power-of-two shift bringing the row maximum into [2^14, 2^15)
+        const int e = (int)((am >> 7) & 0xFF) - 127;
+        const int shift = am ? min(max(14 - e, -100), 100) : 0;
+        const float qs = ldexpf(1.0f, shift);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            u32x4_t hv;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t x = w[4 * kk + k];
+                const float lo = __builtin_bit_cast(float, x << 16) * qs;
+                const float hi = __builtin_bit_cast(float, x & 0xFFFF0000u) * qs;
+                hv[k] = as_u32(half2_t{(_Float16)lo, (_Float16)hi});
+            }
+            qlds[(rt * KK + kk) * 64 + lane] = __builtin_bit_cast(half8_t, hv);
+        }
+        if (g == 0) {
+            const float gk = p.gscale[(b * p.Hkv + kh) * 2 + 0];
+            sm_c[row] = valid ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
+        }
+    }
+    __syncthreads();
+    float cexp[NT];
+    int qi[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        const int row = 16 * rt + n;
+        cexp[rt] = sm_c[row];
+        qi[rt] = row < R ? row / G : p.n_q;          // padded rows see every key (their q is 0)
+    }
+
+    State<D, NT> st;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        st.m[rt] = -INFINITY;
+        st.lsum[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < EPL; ++dt) st.acc[rt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // ---- stream the unit's blocks: wave w takes blocks w, w+4, ...; the next block's K
+    // loads are issued once this block's K is in the S^T tiles, its V loads once this
+    // block's V codes are interleaved, so they overlap the softmax and PV work.
+    Raw<D> r;
+    int kb = wave;
+    Offs o = lane_offsets<D>(base + t0 + (int64_t)kBlockTokens * kb, g, n);
+    constexpr uint32_t kStep = kBlockTokens * kWaves;    // tokens between a wave's blocks
+    if (kb < nblk) {
+        load_k<D>(r, kc, ks, o);
+        load_v<D>(r, vc, vs, o);
+    }
+    // offset limit of the first block of this wave relative to L - n_q (32-bit: tokens < 2^31)
+    int lim = (int)(L - p.n_q - t0) - kBlockTokens * kb;
+    for (; kb < nblk; kb += kWaves, lim -= (int)kStep) {
+        // With more than one row tile the Q fragments are re-read from LDS every block
+        // instead of being held in 32 registers per tile.
+        if constexpr (NT > 1) asm volatile("" ::: "memory");
+        const bool has_next = kb + kWaves < nblk;
+        o.kc += kStep * (D / 2);
+        o.ks += kStep * (D / 16);
+        o.vc += kStep * (D / 2);
+        o.vs += kStep * (D / 16);
+        float4_t s[2][NT];
+        qk_block<D, NT>(s, r, qlds, lane);
+        if (has_next) load_k<D>(r, kc, ks, o);
+        VPrep<D> vp;
+        v_prep<D>(vp, r);
+        if (has_next) load_v<D>(r, vc, vs, o);
+        half8_t pa[NT];
+        softmax_block<D, NT>(st, s, pa, cexp, qi, lim, g);
+        pv_block<D, NT>(st, vp, pa);
+    }
+
+    // ---- merge the four waves' (o, m, l) and write the unit's partial
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        if (g == 0) sm_m[wave][16 * rt + n] = st.m[rt];          // m: row 16 rt + n
+        if (n == 0) {                                             // l: rows 16 rt + 4 g + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm_l[wave][16 * rt + 4 * g + i] = st.lsum[rt][i];
+        }
+    }
+    __syncthreads();                                  // also ends every read of the Q fragments
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * g + i;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][row]);
+            const float mw = sm_m[wave][row];
+            const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+#pragma unroll
+            for (int dt = 0; dt < EPL; ++dt) st.acc[rt][dt][i] *= f;
+        }
+    }
+    float(*buf)[16][LD::STRIDE] = reinterpret_cast<float(*)[16][LD::STRIDE]>(lds);
+    float *ws_o = p.ws_o + (int64_t)u * R * D;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float *dst = &buf[wave][4 * g + i][EPL * n];
+#pragma unroll
+            for (int dt = 0; dt < EPL; dt += 4)
+                *reinterpret_cast<float4_t *>(dst + dt) =
+                    float4_t{st.acc[rt][dt][i], st.acc[rt][dt + 1][i], st.acc[rt][dt + 2][i], st.acc[rt][dt + 3][i]};
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < 16 * D; e += 256) {
+            const int r16 = e / D, d = e - r16 * D;
+            const int row = 16 * rt + r16;
+            if (row < R) {
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) sum += buf[w][r16][d];
+                ws_o[(int64_t)row * D + d] = sum;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x < R) {
+        const int row = threadIdx.x;
+        float M = -INFINITY;
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][row]);
+        float Ls = 0.f;
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = sm_m[w][row];
+            if (mw != -INFINITY) Ls += exp2f(mw - M) * sm_l[w][row];
+        }
+        p.ws_m[(int64_t)u * R + row] = M;
+        p.ws_l[(int64_t)u * R + row] = Ls;
+    }
+}
+
+// One workgroup of D threads per (sequence, KV head, row); thread = output element.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
+    const int R = p.R;
+    const int blk = blockIdx.x;
+    const int r = blk % R;
+    const int bk = blk / R;
+    const int kh = bk % p.Hkv, b = bk / p.Hkv;
+    const int ns = p.n_split[b];
+    const int64_t u0 = (int64_t)p.unit_base[b] + (int64_t)kh * ns;
+    const int d = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.ws_m[(u0 + s) * R + r]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < ns; ++s) {
+        const float ms = p.ws_m[(u0 + s) * R + r];
+        const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+        num += w * p.ws_o[((u0 + s) * R + r) * D + d];
+        den += w * p.ws_l[(u0 + s) * R + r];
+    }
+    // v_hat = (e2m1 * S * 2^-8) * 2^8 * g_V
+    const float o = num / den * (256.0f * p.gscale[(b * p.Hkv + kh) * 2 + 1]);
+    const int i = r / p.G, h = kh * p.G + (r - i * p.G);
+    const int64_t idx = (((int64_t)b * p.n_q + i) * p.Hq + h) * D + d;
+    if (p.out_bf16) {
+        const uint32_t x = __builtin_bit_cast(uint32_t, o);
+        const uint32_t rnd = x + 0x7FFFu + ((x >> 16) & 1u);      // round to nearest even
+        reinterpret_cast<uint16_t *>(p.out)[idx] = (uint16_t)(rnd >> 16);
+    } else {
+        reinterpret_cast<float *>(p.out)[idx] = o;
+    }
+}
+
+template <int D, int NT>
+hipError_t launch_partial_t(const DecodeParams &p, hipStream_t s) {
+    hipLaunchKernelGGL((decode_partial_kernel<D, NT>), dim3(p.units), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream_t s) {
+    if (D == 256) {
+        switch (NT) {
+            case 1: return launch_partial_t<256, 1>(p, s);
+            case 2: return launch_partial_t<256, 2>(p, s);
+            case 3: return launch_partial_t<256, 3>(p, s);
+            case 4: return launch_partial_t<256, 4>(p, s);
+        }
+    } else if (D == 128) {
+        switch (NT) {
+            case 1: return launch_partial_t<128, 1>(p, s);
+            case 2: return launch_partial_t<128, 2>(p, s);
+            case 3: return launch_partial_t<128, 3>(p, s);
+            case 4: return launch_partial_t<128, 4>(p, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_combine(const DecodeParams &p, int D, hipStream_t s) {
+    const unsigned blocks = (unsigned)(p.B * p.Hkv * p.R);
+    if (D == 256)
+        hipLaunchKernelGGL(decode_combine_kernel<256>, dim3(blocks), dim3(256), 0, s, p);
+    else if (D == 128)
+        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(blocks), dim3(128), 0, s, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

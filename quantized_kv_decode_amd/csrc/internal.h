@@ -1,0 +1,69 @@
+// Internal declarations shared by the host API and the kernel launchers.
+// Nothing here is part of the public ABI (include/nvfp4_kv.h is).
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace nvfp4 {
+
+constexpr int kMaxSeqs = 8;
+constexpr int kMaxRows = 64;
+constexpr int kBlockTokens = 32;     // tokens per KV block: one PV MFMA K-step (16x16x32)
+constexpr int kWaves = 4;            // waves per decode workgroup (256 threads)
+constexpr int kCUs = 256;            // compute units the split plan fills (MI355X)
+
+// Split-K plan: sequence b is cut into n_split[b] units of split_len[b] tokens
+// (a multiple of kBlockTokens; the last unit ends at the sequence length), for
+// each KV head. Units are numbered sequence-major, then KV head, then split.
+struct SplitPlan {
+    int32_t B, Hkv, Hq, G, n_q, R, NT, D;
+    int32_t n_split[kMaxSeqs];
+    int32_t split_len[kMaxSeqs];
+    int32_t unit_base[kMaxSeqs];
+    int32_t units;
+};
+
+// Kernel parameters of the decode pair (passed by value).
+struct DecodeParams {
+    const uint8_t *kc, *ks, *vc, *vs;   // pool planes
+    int64_t cap;
+    const float *gscale;                 // [B][Hkv][2]
+    const uint16_t *q;                   // bf16 [B][n_q][Hq][D]
+    float *ws_o, *ws_m, *ws_l;           // [units][R][D], [units][R], [units][R]
+    void *out;
+    int32_t out_bf16;
+    float sm_scale;
+    int32_t B, Hkv, Hq, G, n_q, R;
+    int64_t seq_base[kMaxSeqs];
+    int64_t seq_len[kMaxSeqs];
+    int32_t n_split[kMaxSeqs];
+    int32_t split_len[kMaxSeqs];
+    int32_t unit_base[kMaxSeqs];
+    int32_t units;
+};
+
+struct AppendParams {
+    const uint16_t *k_new, *v_new;       // bf16 [rows][Hkv][D]
+    const float *gscale;                 // [B][Hkv][2]
+    uint8_t *kc, *ks, *vc, *vs;
+    int64_t cap;
+    int32_t B, Hkv, D;
+    int64_t rows;                        // sum of n_new
+    int64_t row_start[kMaxSeqs + 1];     // prefix sums of n_new
+    int64_t dst_start[kMaxSeqs];         // seq_base + write_pos
+};
+
+struct CalibParams {
+    const uint16_t *k_rows, *v_rows;     // bf16 [rows][Hkv][D]
+    float *gscale;                       // [B][Hkv][2]
+    int32_t B, Hkv, D;
+    int64_t row_start[kMaxSeqs + 1];
+};
+
+hipError_t launch_calibrate(const CalibParams &p, hipStream_t s);
+hipError_t launch_append(const AppendParams &p, hipStream_t s);
+hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream_t s);
+hipError_t launch_decode_combine(const DecodeParams &p, int D, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,92 @@
+"""Shared test plumbing: run a workload through the oracle and through the HIP path.
+
+The oracle side and the GPU side only share the seeded inputs from `workloads`.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+# Attention acceptance: max |o_gpu - o_ref| <= TOL_REL * max |V_hat| over the test case.
+TOL_REL = 2e-3
+
+
+class OracleRun:
+    def __init__(self, w: workloads.Workload, k=None, v=None, q=None, nthreads=None):
+        self.w = w
+        self.k = workloads.all_kv_rows(w, "k") if k is None else k          # bf16 [cap][Hkv][D]
+        self.v = workloads.all_kv_rows(w, "v") if v is None else v
+        self.q = workloads.queries(w) if q is None else q
+        ku, vu = workloads.as_u16(self.k), workloads.as_u16(self.v)
+        self.g = oracle.calibrate(ku, vu, w.seq_lens)
+        self.cache = oracle.Cache(w.num_kv_heads, w.head_dim, w.capacity)
+        oracle.append(self.cache, ku, vu, self.g, w.seq_base, [0] * w.batch, list(w.seq_lens), nthreads)
+        self.nthreads = nthreads
+
+    def attention(self, sel=None):
+        return oracle.attention(self.cache, self.g, workloads.as_u16(self.q), self.w.seq_base, self.w.seq_lens,
+                                self.w.n_q, self.w.sm_scale, sel=sel, nthreads=self.nthreads)
+
+    def vmax(self) -> float:
+        """max |V_hat| over every stored V row of the test case."""
+        m = 0.0
+        w = self.w
+        for b in range(w.batch):
+            for h in range(w.num_kv_heads):
+                base, L = w.seq_base[b], w.seq_lens[b]
+                gv = float(self.g[b, h, 1])
+                codes = self.cache.v_codes[h, base:base + L]
+                scales = self.cache.v_scales[h, base:base + L].astype(np.int64)
+                # max |e2m1| per byte is max of the two nibbles' magnitudes; E4M3 scale value
+                mag = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+                lo = mag[codes & 7]
+                hi = mag[(codes >> 4) & 7]
+                emax = np.maximum(lo, hi).reshape(L, -1, 8).max(axis=2)       # per group
+                sval = np.array([oracle.e4m3_value(c) for c in range(256)])[scales]
+                m = max(m, float((emax * sval).max() * gv))
+        return m
+
+
+def gpu_run(w: workloads.Workload, k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, out_dtype=torch.float32,
+            chunk_rows: int | None = None):
+    """Calibrate, append and decode on the GPU through the C ABI. Returns (pool, g, out)."""
+    import quantized_kv_decode_amd as qk
+    dev = "cuda"
+    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev)
+    kd, vd = k.to(dev), v.to(dev)
+    g = qk.calibrate(pool, kd, vd, list(w.seq_lens))
+    if chunk_rows is None:
+        qk.append(pool, kd, vd, g, w.seq_base, [0] * w.batch, list(w.seq_lens))
+    else:
+        for b in range(w.batch):
+            base, L = w.seq_base[b], w.seq_lens[b]
+            for r0 in range(0, L, chunk_rows):
+                r1 = min(L, r0 + chunk_rows)
+                ks = kd[base + r0:base + r1].contiguous()
+                vs = vd[base + r0:base + r1].contiguous()
+                n_new = [0] * w.batch
+                n_new[b] = r1 - r0
+                wp = [0] * w.batch
+                wp[b] = r0
+                qk.append(pool, ks, vs, g, w.seq_base, wp, n_new)
+    del kd, vd
+    out = qk.decode_attn(pool, g, q.to(dev), w.seq_base, list(w.seq_lens), w.sm_scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return pool, g, out
+
+
+def assert_planes_equal(pool, cache: oracle.Cache):
+    for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        got = getattr(pool, name).cpu().numpy()
+        ref = getattr(cache, name)
+        if not np.array_equal(got, ref):
+            bad = np.argwhere(got != ref)
+            i = tuple(bad[0])
+            raise AssertionError(f"{name}: {len(bad)} bytes differ; first at {i}: gpu {got[i]:#04x} oracle {ref[i]:#04x}")
+
+
+def max_err(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.abs(got.astype(np.float64) - ref).max())

@@ -1,0 +1,125 @@
+"""The C ABI library loads, exports what include/*.h declares, and validates
+arguments on the host (every call below fails validation before any HIP call,
+so these tests need no GPU)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(nvfp4_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import quantized_kv_decode_amd as qk
+    if not os.path.exists(qk.LIB_PATH):
+        pytest.fail("libnvfp4kv.so not built (run __graft_entry__.build())")
+    return qk.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn_workspace_bytes", "nvfp4_decode_attn",
+              "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine", "nvfp4_last_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names
+    for f in names:
+        assert hasattr(lib, f), f
+
+
+class _FakeTensor:
+    """Stands in for a device tensor: only an aligned address is needed for validation."""
+    def __init__(self, addr, n=0):
+        self._a, self._n = addr, n
+
+    def data_ptr(self):
+        return self._a
+
+    def numel(self):
+        return self._n
+
+
+def _desc(qk, H=4, D=256, cap=1000, addr=0x100000):
+    return qk.CacheDesc(addr, addr + 0x10000, addr + 0x20000, addr + 0x30000, H, D, cap)
+
+
+def _call_decode(qk, lib, d, B=1, lens=(100,), base=(0,), n_q=1, Hq=24, ws=1 << 30, out_dtype=0, q=0x200000,
+                 out=0x300000, g=0x400000, wsp=0x500000, sm=0.0625):
+    return lib.nvfp4_decode_attn(ctypes.byref(d) if d is not None else None, g, q, out, out_dtype, B, qk._i64(base),
+                                 qk._i64(lens), n_q, Hq, sm, wsp, ws, None)
+
+
+def test_decode_validation_codes(lib):
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk)
+    assert _call_decode(qk, lib, None) == qk.EINVAL
+    assert "null" in lib.nvfp4_last_error().decode()
+    assert _call_decode(qk, lib, _desc(qk, D=64)) == qk.EUNSUPPORTED
+    assert _call_decode(qk, lib, _desc(qk, H=0)) == qk.EINVAL
+    assert _call_decode(qk, lib, _desc(qk, addr=0x100008)) == qk.EINVAL          # unaligned plane
+    assert _call_decode(qk, lib, d, Hq=25) == qk.EUNSUPPORTED                      # Hq % Hkv
+    assert _call_decode(qk, lib, d, n_q=11) == qk.EUNSUPPORTED                     # 6 x 11 rows > 64
+    assert _call_decode(qk, lib, d, n_q=0) == qk.EINVAL
+    assert _call_decode(qk, lib, d, B=0) == qk.EINVAL
+    assert _call_decode(qk, lib, d, B=9, lens=[10] * 9, base=[0] * 9) == qk.EUNSUPPORTED
+    assert _call_decode(qk, lib, d, lens=(0,)) == qk.ERANGE                        # shorter than n_q
+    assert _call_decode(qk, lib, d, lens=(1001,)) == qk.ERANGE                     # past capacity
+    assert _call_decode(qk, lib, d, base=(950,)) == qk.ERANGE                      # slots past capacity
+    assert _call_decode(qk, lib, d, ws=16) == qk.EWORKSPACE
+    assert _call_decode(qk, lib, d, out_dtype=7) == qk.EINVAL
+    assert _call_decode(qk, lib, d, q=0) == qk.EINVAL
+    assert _call_decode(qk, lib, d, q=0x200004) == qk.EINVAL
+    assert _call_decode(qk, lib, d, g=0) == qk.EINVAL
+    assert _call_decode(qk, lib, d, sm=float("nan")) == qk.EINVAL
+
+
+def test_append_and_calibrate_validation_codes(lib):
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk)
+    i64 = qk._i64
+    a = 0x600000
+    # empty append is a no-op success, with or without row pointers
+    assert lib.nvfp4_kv_append(ctypes.byref(d), None, None, a, 1, i64([0]), i64([0]), i64([0]), None) == qk.OK
+    assert lib.nvfp4_kv_append(ctypes.byref(d), a, a, a, 1, i64([0]), i64([990]), i64([11]), None) == qk.ERANGE
+    assert lib.nvfp4_kv_append(ctypes.byref(d), a, a, a, 1, i64([0]), i64([-1]), i64([1]), None) == qk.ERANGE
+    assert lib.nvfp4_kv_append(ctypes.byref(d), a, a, a, 1, i64([0]), i64([0]), i64([-1]), None) == qk.EINVAL
+    assert lib.nvfp4_kv_append(ctypes.byref(d), a, a, 0, 1, i64([0]), i64([0]), i64([1]), None) == qk.EINVAL
+    assert lib.nvfp4_kv_append(ctypes.byref(d), a + 2, a, a, 1, i64([0]), i64([0]), i64([1]), None) == qk.EINVAL
+    assert lib.nvfp4_kv_append(ctypes.byref(d), a, a, a, 9, i64([0] * 9), i64([0] * 9), i64([1] * 9),
+                               None) == qk.EUNSUPPORTED
+    assert lib.nvfp4_kv_append(ctypes.byref(_desc(qk, D=192)), a, a, a, 1, i64([0]), i64([0]), i64([1]),
+                               None) == qk.EUNSUPPORTED
+    assert lib.nvfp4_kv_calibrate(ctypes.byref(d), a, a, 1, i64([-1]), a, None) == qk.EINVAL
+    assert lib.nvfp4_kv_calibrate(ctypes.byref(d), a, a, 0, i64([1]), a, None) == qk.EINVAL
+    assert lib.nvfp4_kv_calibrate(ctypes.byref(d), a, a, 1, i64([1]), 0, None) == qk.EINVAL
+    assert lib.nvfp4_kv_calibrate(ctypes.byref(d), 0, a, 1, i64([1]), a, None) == qk.EINVAL
+
+
+def test_workspace_query(lib):
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk, cap=10 ** 6)
+    ws = lambda lens, n_q=1, Hq=24: lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), len(lens), qk._i64(lens),
+                                                                          n_q, Hq)
+    assert ws([0]) == 0                                  # invalid arguments -> 0
+    assert ws([100], Hq=25) == 0
+    small, big = ws([100]), ws([400000])
+    assert 0 < small <= big
+    # one split per (sequence, head) at minimum: R x (D + 2) floats each
+    assert small >= 4 * 6 * (256 + 2) * 4
+    # a long sequence is cut into at most two workgroups per CU for one row tile
+    assert big <= 2 * 256 * 6 * (256 + 2) * 4 + 3 * 256

@@ -1,0 +1,307 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Quantiser (calibrate + append): bit-exact bytes. Attention: max |o_gpu - o_ref|
+<= 2e-3 * max |V_hat| over the test case (fp32 accumulation against fp64 over
+the same dequantised KV, which the oracle builds from its own quantiser).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import TOL_REL, OracleRun, assert_planes_equal, gpu_run, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def qk():
+    import quantized_kv_decode_amd as qk
+    qk.load_library()
+    return qk
+
+
+# ---------------------------------------------------------------- quantiser ------
+SMALL = [
+    dict(seq_lens=(200, 77), num_kv_heads=2, num_q_heads=6, head_dim=256, n_q=3),
+    dict(seq_lens=(45,), num_kv_heads=1, num_q_heads=4, head_dim=128, n_q=1, v_dist="laplace"),
+    dict(seq_lens=(300, 1, 64, 33), num_kv_heads=4, num_q_heads=8, head_dim=256, n_q=1, outlier_frac=0.02),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_calibrate_and_append_bit_exact(qk, shape):
+    w = workloads.small(**shape)
+    say("calibrate/append", shape)
+    ref = OracleRun(w)
+    pool, g, _ = gpu_run(w, ref.k, ref.v, ref.q)
+    assert np.array_equal(g.cpu().numpy(), ref.g), "global scales differ"
+    assert_planes_equal(pool, ref.cache)
+
+
+def test_append_in_chunks_at_offsets(qk):
+    w = workloads.small(seq_lens=(130, 70), num_kv_heads=2, num_q_heads=4, head_dim=256, n_q=2)
+    say("chunked append")
+    ref = OracleRun(w)
+    pool, _, _ = gpu_run(w, ref.k, ref.v, ref.q, chunk_rows=17)
+    assert_planes_equal(pool, ref.cache)
+
+
+def _bf16_u16(x):
+    return workloads.as_u16(torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16))
+
+
+def _bf16_neighbours(vals):
+    """Every bf16 value in vals plus the bf16 values one ulp either side."""
+    u = _bf16_u16(vals).astype(np.int32)
+    out = np.concatenate([u, u + 1, np.maximum(u - 1, 0)]) & 0x7FFF
+    sign = np.arange(out.size) % 2 == 1
+    return (out | (sign.astype(np.int32) << 15)).astype(np.uint16)
+
+
+def adversarial_rows(D=256):
+    """Groups whose maxima sit on every E4M3 midpoint (times 6) and whose elements sit
+    on every E2M1 midpoint of their scale, with bf16 neighbours, signed zeros, zero
+    groups and saturating values, for g = 1 (so every tie is representable)."""
+    e4 = [oracle.e4m3_value(c) for c in range(127)]
+    groups = []
+    for k in range(126):                                     # scale ties and their neighbours
+        mid = 0.5 * (e4[k] + e4[k + 1])
+        amax = _bf16_neighbours([6 * mid])
+        for a in amax:
+            grp = np.zeros(16, np.uint16)
+            grp[0] = a
+            grp[1] = _bf16_u16([-mid])[0]
+            groups.append(grp)
+    thr = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 3.0, 6.0]
+    for c in (1, 2, 7, 8, 0x30, 0x38, 0x3A, 0x55, 0x70, 0x7E):   # element ties under several scales
+        S = e4[c]
+        vals = _bf16_neighbours([t * S for t in thr])
+        for i in range(0, vals.size, 15):
+            grp = np.zeros(16, np.uint16)
+            grp[0] = _bf16_u16([6 * S])[0]
+            chunk = vals[i:i + 15]
+            grp[1:1 + chunk.size] = chunk
+            groups.append(grp)
+    groups.append(np.zeros(16, np.uint16))                     # +0 group
+    groups.append(np.full(16, 0x8000, np.uint16))              # -0 group
+    groups.append(_bf16_u16([3e4, -3e4, 1e5, 7, -1e-3] + [0] * 11))    # saturating
+    groups.append(_bf16_u16([1e-38, -3e-39, 1e-40] + [0] * 13))        # bf16 subnormals
+    n = len(groups)
+    per_row = D // 16
+    rows = int(math.ceil(n / per_row))
+    flat = np.zeros((rows * per_row, 16), np.uint16)
+    flat[:n] = np.stack(groups)
+    return flat.reshape(rows, D)
+
+
+@pytest.mark.parametrize("gval", [1.0, 0.5, 3.0, 0.0, 1e-30, 7.1e-36, 1e-40, 2.5e30])
+def test_append_adversarial_groups(qk, gval):
+    D = 256
+    rows = adversarial_rows(D)
+    n = rows.shape[0]
+    say("adversarial append", gval, n, "rows")
+    # the same rows for K and V, one KV head, one sequence
+    x = workloads.from_u16(rows).reshape(n, 1, D)
+    g = np.array([[[gval, gval]]], np.float32)
+    ref = oracle.Cache(1, D, n)
+    oracle.append(ref, workloads.as_u16(x), workloads.as_u16(x), g, [0], [0], [n])
+    pool = qk.KVPool(1, D, n)
+    xd = x.cuda()
+    qk.append(pool, xd, xd, torch.from_numpy(g).cuda(), [0], [0], [n])
+    torch.cuda.synchronize()
+    assert_planes_equal(pool, ref)
+
+
+def test_calibrate_edge_values(qk):
+    D = 128
+    say("calibrate edges")
+    rows = np.zeros((3, 2, D), np.uint16)        # seq 0: 1 row all zero; seq 1: 2 rows
+    rows[1, 0, 5] = _bf16_u16([-2688.0])[0]
+    rows[2, 1, 7] = _bf16_u16([1e-38])[0]
+    rows[2, 0, 9] = _bf16_u16([3.3e38])[0]
+    x = workloads.from_u16(rows)
+    ref = oracle.calibrate(rows, rows, [1, 2])
+    pool = qk.KVPool(2, D, 8)
+    g = qk.calibrate(pool, x.cuda(), x.cuda(), [1, 2])
+    assert np.array_equal(g.cpu().numpy(), ref)
+    # a sequence with no rows gets g = 0
+    g0 = qk.calibrate(pool, x.cuda(), x.cuda(), [0, 3])
+    assert np.array_equal(g0.cpu().numpy(), oracle.calibrate(rows, rows, [0, 3]))
+
+
+# ---------------------------------------------------------------- attention ------
+DECODE_SHAPES = [
+    dict(seq_lens=(512,), num_kv_heads=1, num_q_heads=4, head_dim=128, n_q=1),
+    dict(seq_lens=(1000, 77, 3), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=1),
+    dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=4, v_dist="laplace"),   # 24 rows
+    dict(seq_lens=(963,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6, outlier_frac=0.02),        # 36 rows
+    dict(seq_lens=(6, 7, 31, 32, 33), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6),
+    dict(seq_lens=(2050,), num_kv_heads=2, num_q_heads=2, head_dim=128, n_q=5),                            # G = 1
+    dict(seq_lens=(333, 100), num_kv_heads=1, num_q_heads=16, head_dim=256, n_q=4),                       # 64 rows
+    dict(seq_lens=(257,), num_kv_heads=1, num_q_heads=8, head_dim=128, n_q=6),                            # 48 rows
+]
+
+
+def _check_decode(w, ref, out, sel=None):
+    got = out.float().cpu().numpy()
+    if sel is None:
+        exp = ref.attention()
+    else:
+        exp = ref.attention(sel)
+        got = np.stack([got[b, i, h] for (b, i, h) in sel])
+    tol = TOL_REL * ref.vmax()
+    err = max_err(got, exp)
+    say(f"  max err {err:.3e}  tol {tol:.3e}  ({err / tol * 100:.2f}% of budget)")
+    assert err <= tol
+    return err
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES)
+def test_decode_matches_oracle(qk, shape):
+    w = workloads.small(**shape)
+    say("decode", shape)
+    ref = OracleRun(w)
+    pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
+    assert_planes_equal(pool, ref.cache)
+    _check_decode(w, ref, out)
+    # bf16 output is the round-to-nearest-even of the fp32 result
+    outb = qk.decode_attn(pool, g, ref.q.cuda(), w.seq_base, list(w.seq_lens), w.sm_scale, out_dtype=torch.bfloat16)
+    assert torch.equal(outb, out.to(torch.bfloat16))
+
+
+def test_decode_deterministic_and_partial_combine_split(qk):
+    w = workloads.small(seq_lens=(5000, 1234), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=6)
+    say("determinism")
+    ref = OracleRun(w)
+    pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
+    q = ref.q.cuda()
+    out2 = qk.decode_attn(pool, g, q, w.seq_base, list(w.seq_lens), w.sm_scale)
+    assert torch.equal(out, out2)
+    ws = qk.alloc_workspace(pool, list(w.seq_lens), w.n_q, w.num_q_heads)
+    out3 = torch.empty_like(out)
+    qk.decode_attn_partial(pool, g, q, w.seq_base, list(w.seq_lens), w.sm_scale, ws)
+    qk.decode_attn_combine(pool, g, out3, list(w.seq_lens), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out3)
+    _check_decode(w, ref, out)
+
+
+def test_split_plan_invariance(qk):
+    """Sequence 0 decoded alone and next to a much longer sequence gets a different
+    split plan; the results agree to fp32 noise and both pass the oracle check."""
+    w = workloads.small(seq_lens=(3000, 60000), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=2)
+    say("split invariance")
+    ref = OracleRun(w)
+    pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
+    q0 = ref.q[:1].cuda()
+    g0 = g[:1].contiguous()
+    alone = qk.decode_attn(pool, g0, q0, [0], [3000], w.sm_scale)
+    torch.cuda.synchronize()
+    vmax = ref.vmax()
+    assert (alone[0] - out[0]).abs().max().item() <= 1e-5 * vmax
+    _check_decode(w, ref, out, sel=[(b, i, h) for b in range(2) for i in range(2) for h in range(0, 12, 5)])
+
+
+def test_extreme_scores_and_constant_v(qk):
+    """Large queries (scores spanning thousands of units: the lazy running-max path
+    and its rescale) and V constant per head (output must be that constant)."""
+    w = workloads.small(seq_lens=(4000,), num_kv_heads=2, num_q_heads=8, head_dim=256, n_q=3)
+    say("extreme scores")
+    k = workloads.all_kv_rows(w, "k")
+    v = torch.zeros_like(k)
+    v[:, 0] = 1.5
+    v[:, 1] = -0.75
+    q = (workloads.queries(w).float() * 40).to(torch.bfloat16)
+    ref = OracleRun(w, k=k, v=v, q=q)
+    pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
+    _check_decode(w, ref, out)
+    o = out.cpu()
+    assert torch.allclose(o[:, :, :4], torch.full_like(o[:, :, :4], 1.5), rtol=0, atol=1e-6)
+    assert torch.allclose(o[:, :, 4:], torch.full_like(o[:, :, 4:], -0.75), rtol=0, atol=1e-6)
+
+
+def test_sequence_at_pool_end_and_zero_kv(qk):
+    """A sequence ending exactly at the pool's last slot with a ragged tail (reads past
+    the end stay in bounds), all-zero K (uniform weights) and all-zero V."""
+    w = workloads.small(seq_lens=(37, 101), num_kv_heads=1, num_q_heads=4, head_dim=128, n_q=2)
+    say("pool end / zero kv")
+    k = torch.zeros((w.capacity, 1, 128), dtype=torch.bfloat16)
+    v = workloads.all_kv_rows(w, "v")
+    ref = OracleRun(w, k=k, v=v)
+    pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
+    _check_decode(w, ref, out)
+    ref0 = OracleRun(w, k=workloads.all_kv_rows(w, "k"), v=torch.zeros_like(k))
+    pool0, g0, out0 = gpu_run(w, ref0.k, ref0.v, ref0.q)
+    assert torch.count_nonzero(out0).item() == 0
+
+
+def test_workspace_too_small_is_rejected(qk):
+    w = workloads.small(seq_lens=(100,), num_kv_heads=1, num_q_heads=4, head_dim=128, n_q=1)
+    pool = qk.KVPool(1, 128, 100)
+    g = torch.zeros((1, 1, 2), device="cuda")
+    q = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qk.Nvfp4Error) as e:
+        qk.decode_attn(pool, g, q, [0], [100], 0.1, workspace=ws)
+    assert e.value.code == qk.EWORKSPACE
+
+
+# ------------------------------------------------------- full-size workloads ------
+def _sample_rows(w, per_head_rows):
+    rng = np.random.default_rng(w.index)
+    sel = []
+    for b in range(w.batch):
+        for h in range(w.num_q_heads):
+            for i in rng.choice(w.n_q, size=min(per_head_rows, w.n_q), replace=False):
+                sel.append((b, int(i), h))
+    return sel
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,per_head", [("tiny", None), ("decode_27b", None), ("mtp_verify", 3),
+                                           ("long_agentic", 1)])
+def test_full_workload(qk, name, per_head):
+    w = workloads.get(name)
+    say("full workload", name, w.seq_lens)
+    ref = OracleRun(w)
+    say("  oracle quantised; running GPU")
+    pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
+    assert np.array_equal(g.cpu().numpy(), ref.g)
+    assert_planes_equal(pool, ref.cache)
+    say("  planes bit-exact; oracle attention")
+    sel = None if per_head is None else _sample_rows(w, per_head)
+    if name == "long_agentic":
+        sel = sel[::3]
+    _check_decode(w, ref, out, sel=sel)
+
+
+@pytest.mark.timeout(900)
+def test_full_append_max_context(qk):
+    """600000-token cache: the first 591808 rows appended, then the timed 8192-row
+    prefill chunk at positions 591808..599999, then decode over all 600000."""
+    w = workloads.get("append_max_context")
+    say("full workload append_max_context")
+    ref = OracleRun(w)
+    import quantized_kv_decode_amd as qk_
+    dev = "cuda"
+    pool = qk_.KVPool(w.num_kv_heads, w.head_dim, w.capacity)
+    kd, vd = ref.k.to(dev), ref.v.to(dev)
+    g = qk_.calibrate(pool, kd, vd, [w.capacity])
+    L0 = w.capacity - w.append_rows
+    qk_.append(pool, kd[:L0].contiguous(), vd[:L0].contiguous(), g, [0], [0], [L0])
+    qk_.append(pool, kd[L0:].contiguous(), vd[L0:].contiguous(), g, [0], [L0], [w.append_rows])
+    del kd, vd
+    out = qk_.decode_attn(pool, g, ref.q.to(dev), [0], [w.capacity], w.sm_scale)
+    torch.cuda.synchronize()
+    assert_planes_equal(pool, ref.cache)
+    _check_decode(w, ref, out)
