@@ -104,6 +104,9 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_27b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB (read + write) before timing, as a "
+                         "reference dispatch of known size for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -172,6 +175,15 @@ def main() -> int:
         k_append(p)
         k_partial(p)
         k_combine(p)
+
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read + {n} bytes written in one copy dispatch")
+        del src, dst
 
     # ---- warmup (eager) and the reference output of the eager path
     for i in range(W):
