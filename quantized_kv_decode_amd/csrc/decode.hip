@@ -350,6 +350,16 @@ void decode_partial_kernel(DecodeParams p) {
     const rsrc_t vs = plane_rsrc(p.vs + (int64_t)kh * scale_bytes, scale_bytes);
     half8_t *qlds = reinterpret_cast<half8_t *>(lds);
 
+    // The first block's loads go out before the Q prologue so both latencies overlap.
+    Raw<D> r;
+    int kb = wave;
+    Offs o = lane_offsets<D>(base + t0 + (int64_t)kBlockTokens * kb, g, n);
+    constexpr uint32_t kStep = kBlockTokens * kWaves;    // tokens between a wave's blocks
+    if (kb < nblk) {
+        load_k<D>(r, kc, ks, o);
+        load_v<D>(r, vc, vs, o);
+    }
+
     // ---- Q rows -> fp16 fragments in LDS (wave rt converts row tile rt):
     // fragment (rt, kk, lane (g, n)) = row 16 rt + n, d in [QD g + 8 kk, QD g + 8 kk + 8)
     if (wave < NT) {
@@ -418,14 +428,6 @@ void decode_partial_kernel(DecodeParams p) {
     // ---- stream the unit's blocks: wave w takes blocks w, w+4, ...; the next block's K
     // loads are issued once this block's K is in the S^T tiles, its V loads once this
     // block's V codes are interleaved, so they overlap the softmax and PV work.
-    Raw<D> r;
-    int kb = wave;
-    Offs o = lane_offsets<D>(base + t0 + (int64_t)kBlockTokens * kb, g, n);
-    constexpr uint32_t kStep = kBlockTokens * kWaves;    // tokens between a wave's blocks
-    if (kb < nblk) {
-        load_k<D>(r, kc, ks, o);
-        load_v<D>(r, vc, vs, o);
-    }
     // offset limit of the first block of this wave relative to L - n_q (32-bit: tokens < 2^31)
     int lim = (int)(L - p.n_q - t0) - kBlockTokens * kb;
     for (; kb < nblk; kb += kWaves, lim -= (int)kStep) {
@@ -511,9 +513,14 @@ void decode_partial_kernel(DecodeParams p) {
     }
 }
 
-// One workgroup of D threads per (sequence, KV head, row); thread = output element.
+// One 256-thread workgroup per (sequence, KV head, row). Wave w merges units
+// w, w + 4, ... of that (sequence, head); lane c owns the D/64 contiguous outputs
+// [c D/64, (c + 1) D/64). The four wave results are merged through LDS. Every sum
+// runs in a fixed order, so the result does not depend on timing.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
+    constexpr int PER = D / 64;                       // outputs per lane
+    typedef float vecf __attribute__((ext_vector_type(PER)));
     const int R = p.R;
     const int blk = blockIdx.x;
     const int r = blk % R;
@@ -521,26 +528,51 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
     const int kh = bk % p.Hkv, b = bk / p.Hkv;
     const int ns = p.n_split[b];
     const int64_t u0 = (int64_t)p.unit_base[b] + (int64_t)kh * ns;
-    const int d = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const float *mrow = p.ws_m + u0 * R + r;          // m of unit s at mrow[s * R]
+    const float *lrow = p.ws_l + u0 * R + r;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.ws_m[(u0 + s) * R + r]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float ms = p.ws_m[(u0 + s) * R + r];
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, mrow[(int64_t)s * R]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    vecf acc = {};
+    float den = 0.f;
+    const float *orow = p.ws_o + (u0 * R + r) * D + PER * lane;
+#pragma unroll 4
+    for (int s = wave; s < ns; s += kWaves) {
+        const float ms = mrow[(int64_t)s * R];
         const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-        num += w * p.ws_o[((u0 + s) * R + r) * D + d];
-        den += w * p.ws_l[(u0 + s) * R + r];
+        const vecf o = *reinterpret_cast<const vecf *>(orow + (int64_t)s * R * D);
+        acc += w * o;
+        den += w * lrow[(int64_t)s * R];
     }
-    // v_hat = (e2m1 * S * 2^-8) * 2^8 * g_V
-    const float o = num / den * (256.0f * p.gscale[(b * p.Hkv + kh) * 2 + 1]);
-    const int i = r / p.G, h = kh * p.G + (r - i * p.G);
-    const int64_t idx = (((int64_t)b * p.n_q + i) * p.Hq + h) * D + d;
-    if (p.out_bf16) {
-        const uint32_t x = __builtin_bit_cast(uint32_t, o);
-        const uint32_t rnd = x + 0x7FFFu + ((x >> 16) & 1u);      // round to nearest even
-        reinterpret_cast<uint16_t *>(p.out)[idx] = (uint16_t)(rnd >> 16);
-    } else {
-        reinterpret_cast<float *>(p.out)[idx] = o;
+    __shared__ vecf part[kWaves][64];
+    __shared__ float dpart[kWaves];
+    part[wave][lane] = acc;
+    if (lane == 0) dpart[wave] = den;
+    __syncthreads();
+    if (wave == 0) {
+        vecf o = part[0][lane];
+        float dd = dpart[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            o += part[w][lane];
+            dd += dpart[w];
+        }
+        // v_hat = (e2m1 * S * 2^-8) * 2^8 * g_V
+        o *= 256.0f * p.gscale[(b * p.Hkv + kh) * 2 + 1] / dd;
+        const int i = r / p.G, h = kh * p.G + (r - i * p.G);
+        const int64_t idx = (((int64_t)b * p.n_q + i) * p.Hq + h) * D + PER * lane;
+        if (p.out_bf16) {
+            // IEEE conversion: round to nearest even (v_cvt_pk_bf16_f32)
+            typedef __bf16 vecb __attribute__((ext_vector_type(PER)));
+            vecb ob;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) ob[k] = (__bf16)o[k];
+            *reinterpret_cast<vecb *>(reinterpret_cast<__bf16 *>(p.out) + idx) = ob;
+        } else {
+            *reinterpret_cast<vecf *>(reinterpret_cast<float *>(p.out) + idx) = o;
+        }
     }
 }
 
@@ -576,7 +608,7 @@ hipError_t launch_decode_combine(const DecodeParams &p, int D, hipStream_t s) {
     if (D == 256)
         hipLaunchKernelGGL(decode_combine_kernel<256>, dim3(blocks), dim3(256), 0, s, p);
     else if (D == 128)
-        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(blocks), dim3(128), 0, s, p);
+        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(blocks), dim3(256), 0, s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
