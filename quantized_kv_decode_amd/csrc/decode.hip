@@ -71,9 +71,16 @@ __device__ inline uint32_t hmul2(uint32_t a, uint32_t b) { return as_u32(as_h2(a
 
 __device__ inline uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
 
-__device__ inline float wave_max_g(float x) {    // max over the four lane groups (lanes n, n+16, n+32, n+48)
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+// max over the four lane groups (lanes n, n+16, n+32, n+48), on the VALU: permlane16_swap of
+// x with itself yields rows (0,0,2,2) and (1,1,3,3); permlane32_swap of y with itself yields
+// halves (lo,lo) and (hi,hi).
+__device__ inline float wave_max_g(float x) {
+    const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+    const float y = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    const uint32_t yb = __builtin_bit_cast(uint32_t, y);
+    const auto c = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)c[0]), __builtin_bit_cast(float, (uint32_t)c[1]));
 }
 
 template <int D>
@@ -266,7 +273,7 @@ __device__ inline void softmax_block(State<D, NT> &st, const float4_t (&s)[2][NT
         const float mu = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = exp2f(x[rt][j] - mu);
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(x[rt][j] - mu);   // v_exp_f32
         pa[rt] = half8_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
                          (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
     }
