@@ -66,7 +66,9 @@ extern "C" {
 #define NVFP4_MAX_ROWS 64        /* GQA group x query tokens sharing one KV head      */
 
 /* The caller-owned pool. head_dim must be 128 or 256; num_kv_heads >= 1;
- * capacity >= 1 token slots per head plane. */
+ * capacity >= 1 token slots per head plane, and capacity * head_dim / 2 (one
+ * head's code plane in bytes) at most 2^31 - 1, since kernels address a head
+ * plane with 32-bit offsets (else NVFP4_EUNSUPPORTED). */
 typedef struct nvfp4_kv_cache {
     void   *k_codes;
     void   *k_scales;

@@ -41,6 +41,10 @@ int check_cache(const nvfp4_kv_cache *c) {
     if (c->capacity < 1) return fail(NVFP4_EINVAL, "capacity must be >= 1");
     if (c->head_dim != 128 && c->head_dim != 256)
         return fail(NVFP4_EUNSUPPORTED, "head_dim %d unsupported (128 or 256)", c->head_dim);
+    // kernels address one head plane with 32-bit byte offsets
+    if (c->capacity > (int64_t)INT32_MAX / (c->head_dim / 2))
+        return fail(NVFP4_EUNSUPPORTED, "capacity %lld too large: a head's code plane must stay below 2^31 bytes",
+                    (long long)c->capacity);
     return NVFP4_OK;
 }
 
@@ -87,10 +91,11 @@ int make_plan(const nvfp4_kv_cache *c, int32_t num_seqs, const int64_t *seq_base
     pl.R = G * n_q;
     pl.NT = (pl.R + 15) / 16;
     pl.D = c->head_dim;
-    // Fill every CU once: two resident workgroups per CU when one row tile keeps the
-    // register budget small, one otherwise. Splits go greedily to the sequence whose
-    // units are currently longest, so ragged batches get near-equal units.
-    const int64_t slots = std::max<int64_t>((int64_t)nvfp4::kCUs * (pl.NT == 1 ? 2 : 1), (int64_t)num_seqs * pl.Hkv);
+    // Fill every CU once, with as many workgroups as the kernel for NT row tiles keeps
+    // resident. Splits go greedily to the sequence whose units are currently longest,
+    // so ragged batches get near-equal units.
+    const int64_t slots = std::max<int64_t>((int64_t)nvfp4::kCUs * nvfp4::decode_wgs_per_cu(pl.NT),
+                                            (int64_t)num_seqs * pl.Hkv);
     int64_t nsp[nvfp4::kMaxSeqs];
     for (int b = 0; b < num_seqs; ++b) nsp[b] = 1;
     int64_t total = (int64_t)num_seqs * pl.Hkv;

@@ -43,45 +43,12 @@
 #include <stdint.h>
 #include <math.h>
 
-#include "internal.h"
+#include "decode_common.h"
 
 namespace nvfp4 {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyMax = 8.0f;      // raise the softmax reference only past m + 8 (base 2)
-
-__device__ inline half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
-__device__ inline uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
-
-// fp16 pair (S * 2^-8, S * 2^-8) from an E4M3 byte 0x00..0x7E.
-__device__ inline uint32_t scale_pair(uint32_t byte) { return (byte << 7) | (byte << 23); }
-
-template <int SEL>
-__device__ inline uint32_t fp4x2(uint32_t w) {
-    return as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
-}
-
-__device__ inline uint32_t hmul2(uint32_t a, uint32_t b) { return as_u32(as_h2(a) * as_h2(b)); }
-
-__device__ inline uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
-
-// max over the four lane groups (lanes n, n+16, n+32, n+48), on the VALU: permlane16_swap of
-// x with itself yields rows (0,0,2,2) and (1,1,3,3); permlane32_swap of y with itself yields
-// halves (lo,lo) and (hi,hi).
-__device__ inline float wave_max_g(float x) {
-    const uint32_t xb = __builtin_bit_cast(uint32_t, x);
-    const auto a = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
-    const float y = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
-    const uint32_t yb = __builtin_bit_cast(uint32_t, y);
-    const auto c = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)c[0]), __builtin_bit_cast(float, (uint32_t)c[1]));
-}
+using namespace dev;
 
 template <int D>
 struct Raw {
@@ -92,21 +59,6 @@ struct Raw {
     uint32_t ks[2];                               // K scale bytes (D/64 of them) per tile
     uint32_t v[8][VW];                            // 8 tokens (k-slots) per lane
     uint32_t vs[8];                               // V scale byte per token
-};
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer over one head plane: loads past its end return zeros (no fault).
-__device__ inline rsrc_t plane_rsrc(const uint8_t *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Byte offsets of one lane's first load in each stream for the block starting at
-// slot `slot0` (= seq_base + block start); later tokens of the block are
-// immediate offsets. Tokens past the sequence end are read (finite values, or
-// zeros past the plane) and masked out of the softmax.
-struct Offs {
-    uint32_t kc, ks, vc, vs;
 };
 
 template <int D>
@@ -214,27 +166,42 @@ __device__ inline void v_prep(VPrep<D> &vp, const Raw<D> &r) {
         // (masked, p = 0) must stay finite so 0 * v stays 0.
         vp.SP[kp] = ((r.vs[2 * kp] & 0x7Fu) << 7) | ((r.vs[2 * kp + 1] & 0x7Fu) << 23);
     }
+    // Materialise the interleaved words here: otherwise they are computed next to their
+    // use in the PV step, the raw V words stay live across the next block's V loads, and
+    // those loads need fresh registers plus copies (and a wait) at the loop end.
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+#pragma unroll
+        for (int h = 0; h < VW; ++h) asm volatile("" : "+v"(vp.E[kp][h]), "+v"(vp.O[kp][h]));
+        asm volatile("" : "+v"(vp.SP[kp]));
+    }
 }
 
 // Scores -> probabilities for one block. lim = L - n_q - tb: key at offset o of the
 // block is visible to query token i iff o <= lim + i (bottom-right causal; offsets
-// past the sequence end are never visible). Blocks with lim >= 31 need no mask.
-template <int D, int NT, bool MASK>
+// past the sequence end are never visible). Blocks with lim >= 31 need no mask; the
+// mask is applied in place, so both cases leave the scores in the same registers.
+template <int D, int NT>
 __device__ inline void scores_block(float (&x)[NT][8], float (&mrow)[NT], const float4_t (&s)[2][NT],
                                     const float (&cexp)[NT], const int (&qi)[NT], int lim, int g) {
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-        float mloc = -INFINITY;
+    for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float v = s[j >> 2][rt][j & 3] * cexp[rt];
-            if constexpr (MASK) {
+        for (int j = 0; j < 8; ++j) x[rt][j] = s[j >> 2][rt][j & 3] * cexp[rt];
+    if (lim < kBlockTokens - 1) {
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
                 const int o = 16 * (j >> 2) + 4 * g + (j & 3);
-                if (o > lim + qi[rt]) v = -INFINITY;
+                if (o > lim + qi[rt]) x[rt][j] = -INFINITY;
             }
-            x[rt][j] = v;
-            mloc = fmaxf(mloc, v);
-        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        float mloc = x[rt][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, x[rt][j]);
         mrow[rt] = wave_max_g(mloc);
     }
 }
@@ -244,10 +211,7 @@ __device__ inline void softmax_block(State<D, NT> &st, const float4_t (&s)[2][NT
                                      const float (&cexp)[NT], const int (&qi)[NT], int lim, int g) {
     constexpr int EPL = D / 16;
     float x[NT][8], mrow[NT];
-    if (lim >= kBlockTokens - 1)
-        scores_block<D, NT, false>(x, mrow, s, cexp, qi, lim, g);
-    else
-        scores_block<D, NT, true>(x, mrow, s, cexp, qi, lim, g);
+    scores_block<D, NT>(x, mrow, s, cexp, qi, lim, g);
     bool need_any = false;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) need_any |= mrow[rt] > st.m[rt] + kLazyMax;
@@ -320,11 +284,10 @@ struct Lds {
 };
 
 template <int D, int NT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_wgs_per_cu(NT))))
 void decode_partial_kernel(DecodeParams p) {
     constexpr int KK = D / 32;
     constexpr int EPL = D / 16;
-    constexpr int QD = D / 4;
     using LD = Lds<D, NT>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LD::BYTES];
     __shared__ float sm_c[kMaxRows];
@@ -332,17 +295,9 @@ void decode_partial_kernel(DecodeParams p) {
     __shared__ float sm_l[kWaves][kMaxRows];
 
     const int u = blockIdx.x;
-    int b = 0;
-#pragma unroll
-    for (int s = 1; s < kMaxSeqs; ++s)
-        if (s < p.B && u >= p.unit_base[s]) b = s;
-    const int local = u - p.unit_base[b];
-    const int kh = local / p.n_split[b];
-    const int sp = local - kh * p.n_split[b];
-    const int64_t L = p.seq_len[b];
-    const int64_t t0 = (int64_t)sp * p.split_len[b];
-    const int64_t t1 = min(t0 + (int64_t)p.split_len[b], L);
-    const int nblk = (int)((t1 - t0 + kBlockTokens - 1) / kBlockTokens);
+    const Unit un = unit_of(p, u);
+    const int b = un.b, kh = un.kh, nblk = un.nblk;
+    const int64_t L = un.L, t0 = un.t0;
 
     // wave index is uniform across the wave; readfirstlane lets the compiler keep the
     // block loop on the scalar unit
@@ -362,57 +317,14 @@ void decode_partial_kernel(DecodeParams p) {
     int kb = wave;
     Offs o = lane_offsets<D>(base + t0 + (int64_t)kBlockTokens * kb, g, n);
     constexpr uint32_t kStep = kBlockTokens * kWaves;    // tokens between a wave's blocks
-    if (kb < nblk) {
-        load_k<D>(r, kc, ks, o);
-        load_v<D>(r, vc, vs, o);
+    {
+        const Offs o0 = kb < nblk ? o : Offs{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
+        load_k<D>(r, kc, ks, o0);
+        load_v<D>(r, vc, vs, o0);
     }
 
-    // ---- Q rows -> fp16 fragments in LDS (wave rt converts row tile rt):
-    // fragment (rt, kk, lane (g, n)) = row 16 rt + n, d in [QD g + 8 kk, QD g + 8 kk + 8)
-    if (wave < NT) {
-        const int rt = wave;
-        const int row = 16 * rt + n;
-        const bool valid = row < R;
-        uint32_t w[KK * 4];
-        if (valid) {
-            const int i = row / G;
-            const int h = kh * G + (row - i * G);
-            const uint16_t *qr = p.q + (((int64_t)b * p.n_q + i) * p.Hq + h) * D + QD * g;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(qr + 8 * kk);
-                w[4 * kk] = v.x; w[4 * kk + 1] = v.y; w[4 * kk + 2] = v.z; w[4 * kk + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < KK * 4; ++k) w[k] = 0u;
-        }
-        uint32_t am = 0;
-#pragma unroll
-        for (int k = 0; k < KK * 4; ++k) am = max(am, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
-        am = max(am, (uint32_t)__shfl_xor((int)am, 16));
-        am = max(am, (uint32_t)__shfl_xor((int)am, 32));
-        // exact power-of-two shift bringing the row maximum into [2^14, 2^15)
-        const int e = (int)((am >> 7) & 0xFF) - 127;
-        const int shift = am ? min(max(14 - e, -100), 100) : 0;
-        const float qs = ldexpf(1.0f, shift);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            u32x4_t hv;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t x = w[4 * kk + k];
-                const float lo = __builtin_bit_cast(float, x << 16) * qs;
-                const float hi = __builtin_bit_cast(float, x & 0xFFFF0000u) * qs;
-                hv[k] = as_u32(half2_t{(_Float16)lo, (_Float16)hi});
-            }
-            qlds[(rt * KK + kk) * 64 + lane] = __builtin_bit_cast(half8_t, hv);
-        }
-        if (g == 0) {
-            const float gk = p.gscale[(b * p.Hkv + kh) * 2 + 0];
-            sm_c[row] = valid ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
-        }
-    }
+    // ---- Q rows -> fp16 fragments in LDS (wave rt converts row tile rt)
+    if (wave < NT) q_prologue<D>(p, b, kh, wave, lane, qlds, sm_c);
     __syncthreads();
     float cexp[NT];
     int qi[NT];
@@ -438,20 +350,28 @@ void decode_partial_kernel(DecodeParams p) {
     // offset limit of the first block of this wave relative to L - n_q (32-bit: tokens < 2^31)
     int lim = (int)(L - p.n_q - t0) - kBlockTokens * kb;
     for (; kb < nblk; kb += kWaves, lim -= (int)kStep) {
-        // With more than one row tile the Q fragments are re-read from LDS every block
-        // instead of being held in 32 registers per tile.
-        if constexpr (NT > 1) asm volatile("" ::: "memory");
-        const bool has_next = kb + kWaves < nblk;
+        // The Q fragments are re-read from LDS every block instead of being held in 32
+        // registers per row tile (registers decide how many waves a SIMD holds).
+        asm volatile("" ::: "memory");
         o.kc += kStep * (D / 2);
         o.ks += kStep * (D / 16);
         o.vc += kStep * (D / 2);
         o.vs += kStep * (D / 16);
+        // The next block's loads are issued unconditionally: past the unit's last block
+        // they take an offset beyond every plane, which the buffer unit answers with zeros
+        // without a memory access. (A conditional load makes the loaded registers a
+        // two-way merge, which costs register copies and a wait for the fresh loads.)
+        const bool has_next = kb + kWaves < nblk;
+        const Offs on = has_next ? o : Offs{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
         float4_t s[2][NT];
         qk_block<D, NT>(s, r, qlds, lane);
-        if (has_next) load_k<D>(r, kc, ks, o);
+        load_k<D>(r, kc, ks, on);
         VPrep<D> vp;
         v_prep<D>(vp, r);
-        if (has_next) load_v<D>(r, vc, vs, o);
+        // keep the V loads below the code interleave, so they land in the registers it
+        // has just read instead of fresh ones that must be copied back at the loop end
+        __builtin_amdgcn_sched_barrier(0);
+        load_v<D>(r, vc, vs, on);
         half8_t pa[NT];
         softmax_block<D, NT>(st, s, pa, cexp, qi, lim, g);
         pv_block<D, NT>(st, vp, pa);
@@ -528,7 +448,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     constexpr int PER = D / 64;                       // outputs per lane
     typedef float vecf __attribute__((ext_vector_type(PER)));
-    const int R = p.R;
+    const int R = p.R, G = p.G;
     const int blk = blockIdx.x;
     const int r = blk % R;
     const int bk = blk / R;
@@ -592,21 +512,9 @@ hipError_t launch_partial_t(const DecodeParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream_t s) {
-    if (D == 256) {
-        switch (NT) {
-            case 1: return launch_partial_t<256, 1>(p, s);
-            case 2: return launch_partial_t<256, 2>(p, s);
-            case 3: return launch_partial_t<256, 3>(p, s);
-            case 4: return launch_partial_t<256, 4>(p, s);
-        }
-    } else if (D == 128) {
-        switch (NT) {
-            case 1: return launch_partial_t<128, 1>(p, s);
-            case 2: return launch_partial_t<128, 2>(p, s);
-            case 3: return launch_partial_t<128, 3>(p, s);
-            case 4: return launch_partial_t<128, 4>(p, s);
-        }
-    }
+    if (NT != 1) return launch_decode_pair(p, D, NT, s);
+    if (D == 256) return launch_partial_t<256, 1>(p, s);
+    if (D == 128) return launch_partial_t<128, 1>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,146 @@
+// Device helpers shared by the decode kernels (fp4/fp16 packing, buffer
+// resources, the query prologue and the split-unit lookup).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "internal.h"
+
+namespace nvfp4 {
+namespace dev {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMax = 8.0f;      // raise the softmax reference only past m + 8 (base 2)
+
+__device__ inline half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ inline uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// fp16 pair (S * 2^-8, S * 2^-8) from an E4M3 byte 0x00..0x7E.
+__device__ inline uint32_t scale_pair(uint32_t byte) { return (byte << 7) | (byte << 23); }
+
+template <int SEL>
+__device__ inline uint32_t fp4x2(uint32_t w) {
+    return as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+}
+
+__device__ inline uint32_t hmul2(uint32_t a, uint32_t b) { return as_u32(as_h2(a) * as_h2(b)); }
+
+__device__ inline uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (a & mask) | (b & ~mask); }
+
+// max over the four lane groups (lanes n, n+16, n+32, n+48), on the VALU: permlane16_swap of
+// x with itself yields rows (0,0,2,2) and (1,1,3,3); permlane32_swap of y with itself yields
+// halves (lo,lo) and (hi,hi).
+__device__ inline float wave_max_g(float x) {
+    const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane16_swap(xb, xb, false, false);
+    const float y = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    const uint32_t yb = __builtin_bit_cast(uint32_t, y);
+    const auto c = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)c[0]), __builtin_bit_cast(float, (uint32_t)c[1]));
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over one head plane: loads past its end return zeros (no fault).
+__device__ inline rsrc_t plane_rsrc(const uint8_t *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Byte offsets of one lane's first load in each stream for the block starting at
+// slot `slot0` (= seq_base + block start); later tokens of the block are
+// immediate offsets. Tokens past the sequence end are read (finite values, or
+// zeros past the plane) and masked out of the softmax.
+struct Offs {
+    uint32_t kc, ks, vc, vs;
+};
+
+// Head planes are below 2^31 bytes (the capacity limit), so this offset, plus any
+// immediate offset of a block's loads, is out of range for every plane.
+constexpr uint32_t kPastPlane = 0x80000000u;
+
+// Unit u of the split plan: sequence b, KV head kh, tokens [t0, t1) of the
+// sequence (length L), nblk 32-token blocks.
+struct Unit {
+    int b, kh, nblk;
+    int64_t L, t0, t1;
+};
+
+__device__ inline Unit unit_of(const DecodeParams &p, int u) {
+    Unit r;
+    r.b = 0;
+#pragma unroll
+    for (int s = 1; s < kMaxSeqs; ++s)
+        if (s < p.B && u >= p.unit_base[s]) r.b = s;
+    const int local = u - p.unit_base[r.b];
+    r.kh = local / p.n_split[r.b];
+    const int sp = local - r.kh * p.n_split[r.b];
+    r.L = p.seq_len[r.b];
+    r.t0 = (int64_t)sp * p.split_len[r.b];
+    r.t1 = min(r.t0 + (int64_t)p.split_len[r.b], r.L);
+    r.nblk = (int)((r.t1 - r.t0 + kBlockTokens - 1) / kBlockTokens);
+    return r;
+}
+
+// Query rows of row tile rt -> fp16 MFMA B-fragments in LDS, run by one wave.
+// Fragment (rt, kk, lane (g, n)) = row 16 rt + n, d in [D/4 g + 8 kk, D/4 g + 8 kk + 8).
+// Each row is scaled by an exact power of two that brings its maximum magnitude to
+// [2^14, 2^15) before the fp16 conversion; sm_c[row] receives the factor that turns an
+// MFMA score back into sm_scale * q . k_hat * log2(e) (including the 2^8 of the
+// dequantised K and g_K). Rows past R get zero fragments and factor 0.
+template <int D>
+__device__ inline void q_prologue(const DecodeParams &p, int b, int kh, int rt, int lane, half8_t *qlds,
+                                  float *sm_c) {
+    constexpr int KK = D / 32;
+    constexpr int QD = D / 4;
+    const int n = lane & 15, g = lane >> 4;
+    const int row = 16 * rt + n;
+    const bool valid = row < p.R;
+    uint32_t w[KK * 4];
+    if (valid) {
+        const int i = row / p.G;
+        const int h = kh * p.G + (row - i * p.G);
+        const uint16_t *qr = p.q + (((int64_t)b * p.n_q + i) * p.Hq + h) * D + QD * g;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(qr + 8 * kk);
+            w[4 * kk] = v.x; w[4 * kk + 1] = v.y; w[4 * kk + 2] = v.z; w[4 * kk + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KK * 4; ++k) w[k] = 0u;
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int k = 0; k < KK * 4; ++k) am = max(am, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 16));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 32));
+    const int e = (int)((am >> 7) & 0xFF) - 127;
+    const int shift = am ? min(max(14 - e, -100), 100) : 0;
+    const float qs = ldexpf(1.0f, shift);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        u32x4_t hv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t x = w[4 * kk + k];
+            const float lo = __builtin_bit_cast(float, x << 16) * qs;
+            const float hi = __builtin_bit_cast(float, x & 0xFFFF0000u) * qs;
+            hv[k] = as_u32(half2_t{(_Float16)lo, (_Float16)hi});
+        }
+        qlds[(rt * KK + kk) * 64 + lane] = __builtin_bit_cast(half8_t, hv);
+    }
+    if (g == 0) {
+        const float gk = p.gscale[(b * p.Hkv + kh) * 2 + 0];
+        sm_c[row] = valid ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
+    }
+}
+
+}  // namespace dev
+}  // namespace nvfp4

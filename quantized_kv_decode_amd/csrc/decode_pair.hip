@@ -1,0 +1,400 @@
+// Split-K decode partial for two to four row tiles (17..64 query rows per KV head):
+// the wave-pair kernel (gfx950).
+//
+// It computes what the single-tile kernel computes (gzenz/ninfer page, "Context and
+// model": attention over K/V stored as E2M1 codes + E4M3 group-16 scales; knoopx/ninfer
+// page, "Capabilities and limits": MTP verification of 1 + 1..5 draft tokens, which
+// with the GQA group gives up to 64 rows per KV head): per unit (sequence, KV head,
+// token range) and query row, the unnormalised o, the running max m and the sum l.
+//
+// Why pairs. With R rows, a wave that owns a whole 32-token block holds R x D fp32
+// accumulators; at three or four row tiles that leaves one wave per SIMD and the
+// compiler moves accumulators between register files every block. Here the two waves
+// of a pair share each block:
+//   S^T = K . Q^T   wave w (0/1) takes the 16-token tile w of the block, all rows,
+//                   full head_dim (same fragment layout as the single-tile kernel);
+//   softmax         each wave reduces its 16 tokens per row; the pair agrees on the
+//                   running reference m through LDS (barrier 1), then each wave
+//                   writes its fp16 probabilities to LDS (barrier 2);
+//   O += P . V      each wave reads the whole 32-token P (its own and its partner's,
+//                   lane for lane: lane (g, n) of wave w holds exactly the k-slots
+//                   4 w .. 4 w + 3 of lane (g, n)'s A operand) and multiplies it into
+//                   its half of head_dim: output column n of local tile t is
+//                   d = (D/16) n + (D/32) w + t, so lane n's V values again sit in one
+//                   scale group (a half group: D/64 code bytes per token).
+// Dequantisation work per token is that of the single-tile kernel; the accumulators
+// per wave are halved. A 256-thread workgroup holds two pairs that take alternate
+// blocks of one unit and merge at the end. Every wave runs the same number of block
+// iterations (a pair with no block left runs a fully masked one on zero data), so the
+// workgroup barriers always match.
+#include "decode_common.h"
+
+namespace nvfp4 {
+namespace {
+
+using namespace dev;
+
+constexpr int kPairs = 2;                       // wave pairs per workgroup
+constexpr uint32_t kPairStep = kBlockTokens * kPairs;   // tokens between a pair's blocks
+
+template <int D>
+struct PairRaw {
+    static constexpr int KW = D / 32;           // K code dwords of one 16-token tile per lane
+    uint32_t k[KW];
+    uint32_t ks;                                // D/64 K scale bytes
+    uint32_t v[8];                              // D/64 V code bytes per k-slot token
+    uint32_t vs[8];                             // V scale byte per k-slot token
+};
+
+template <int D>
+__device__ inline void pair_load_k(PairRaw<D> &r, rsrc_t kc, rsrc_t ks, const Offs &o) {
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, o.kc, 0, 0);
+    r.k[0] = a[0]; r.k[1] = a[1]; r.k[2] = a[2]; r.k[3] = a[3];
+    if constexpr (D == 256) {
+        const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(kc, o.kc + 16, 0, 0);
+        r.k[4] = c[0]; r.k[5] = c[1]; r.k[6] = c[2]; r.k[7] = c[3];
+        r.ks = __builtin_amdgcn_raw_buffer_load_b32(ks, o.ks, 0, 0);
+    } else {
+        r.ks = __builtin_amdgcn_raw_buffer_load_b16(ks, o.ks, 0, 0);
+    }
+}
+
+// k-slot j of lane group g is token 16 (j >> 2) + 4 g + (j & 3) of the block; the lane
+// offsets already hold the 4 g.
+template <int D>
+__device__ inline void pair_load_v(PairRaw<D> &r, rsrc_t vc, rsrc_t vs, const Offs &o) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t dtok = 16 * (j >> 2) + (j & 3);
+        if constexpr (D == 256)
+            r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vc, o.vc + dtok * (D / 2), 0, 0);
+        else
+            r.v[j] = __builtin_amdgcn_raw_buffer_load_b16(vc, o.vc + dtok * (D / 2), 0, 0);
+        r.vs[j] = __builtin_amdgcn_raw_buffer_load_b8(vs, o.vs + dtok * (D / 16), 0, 0);
+    }
+}
+
+// Lane part of the byte offsets of wave w's loads, relative to the block's first slot.
+template <int D>
+__device__ inline Offs pair_lane_offsets(int w, int g, int n) {
+    Offs o;
+    o.kc = (uint32_t)((16 * w + n) * (D / 2) + (D / 8) * g);
+    o.ks = (uint32_t)((16 * w + n) * (D / 16) + (D / 64) * g);
+    o.vc = (uint32_t)(4 * g * (D / 2) + (D / 32) * n + (D / 64) * w);
+    o.vs = (uint32_t)(4 * g * (D / 16) + (D * n) / 256);
+    return o;
+}
+
+__device__ inline Offs add_slot(const Offs &lane, uint32_t slot0, int D) {
+    Offs o;
+    o.kc = lane.kc + slot0 * (uint32_t)(D / 2);
+    o.ks = lane.ks + slot0 * (uint32_t)(D / 16);
+    o.vc = lane.vc + slot0 * (uint32_t)(D / 2);
+    o.vs = lane.vs + slot0 * (uint32_t)(D / 16);
+    return o;
+}
+
+template <int D>
+__device__ inline half8_t pair_dequant_k(const PairRaw<D> &r, int kk) {
+    const uint32_t w = r.k[kk];
+    const uint32_t sp = scale_pair((r.ks >> (8 * (kk >> 1))) & 0xFFu);
+    const u32x4_t a = {hmul2(fp4x2<0>(w), sp), hmul2(fp4x2<1>(w), sp), hmul2(fp4x2<2>(w), sp),
+                       hmul2(fp4x2<3>(w), sp)};
+    return __builtin_bit_cast(half8_t, a);
+}
+
+// V codes of k-slot pairs (2 kp, 2 kp + 1) interleaved nibble-wise: byte b of E holds
+// element 2 b of both tokens, byte b of O element 2 b + 1; SP their fp16 scale pair.
+struct PairVPrep {
+    uint32_t E[4], O[4], SP[4];
+};
+
+template <int D>
+__device__ inline void pair_v_prep(PairVPrep &vp, const PairRaw<D> &r) {
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+        const uint32_t wa = r.v[2 * kp], wb = r.v[2 * kp + 1];
+        vp.E[kp] = bfi(0x0F0F0F0Fu, wa, wb << 4);
+        vp.O[kp] = bfi(0x0F0F0F0Fu, wa >> 4, wb);
+        // bit 7 cleared: bytes read past a sequence's end must stay finite (p = 0 there)
+        vp.SP[kp] = ((r.vs[2 * kp] & 0x7Fu) << 7) | ((r.vs[2 * kp + 1] & 0x7Fu) << 23);
+    }
+    // materialise here so the raw V words die before the next block's V loads
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) asm volatile("" : "+v"(vp.E[kp]), "+v"(vp.O[kp]), "+v"(vp.SP[kp]));
+}
+
+template <int D, int NT>
+struct PairLds {
+    static constexpr int KK = D / 32;
+    static constexpr int HT = D / 32;                              // PV tiles per wave
+    static constexpr int Q_BYTES = NT * KK * 64 * 16;              // Q fragments [NT][KK][lane]
+    static constexpr int MERGE_BYTES = 2 * HT * 64 * 16;           // one row tile of both halves
+    static constexpr int BIG = Q_BYTES > MERGE_BYTES ? Q_BYTES : MERGE_BYTES;
+};
+
+template <int D, int NT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_wgs_per_cu(NT))))
+void decode_pair_kernel(DecodeParams p) {
+    constexpr int KK = D / 32;
+    constexpr int HT = D / 32;          // PV output tiles per wave (half of D/16)
+    constexpr int EPL = D / 16;
+    using LD = PairLds<D, NT>;
+    __shared__ __attribute__((aligned(16))) uint8_t big[LD::BIG];
+    __shared__ __attribute__((aligned(16))) u32x4_t pbuf[kPairs][NT][64];   // (mt 0 | mt 1) fp16 P per lane
+    __shared__ float xmax[kPairs][2][NT * 16];
+    __shared__ float sm_c[kMaxRows];
+    __shared__ float sm_m[kPairs][kMaxRows];
+    __shared__ float sm_l[kPairs][kMaxRows];
+
+    const int u = blockIdx.x;
+    const Unit un = unit_of(p, u);
+    const int b = un.b, kh = un.kh, nblk = un.nblk;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = wave >> 1, w = wave & 1;
+    const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+    const int R = p.R, G = p.G;
+    const uint32_t code_bytes = (uint32_t)(p.cap * (D / 2)), scale_bytes = (uint32_t)(p.cap * (D / 16));
+    const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * code_bytes, code_bytes);
+    const rsrc_t ks = plane_rsrc(p.ks + (int64_t)kh * scale_bytes, scale_bytes);
+    const rsrc_t vc = plane_rsrc(p.vc + (int64_t)kh * code_bytes, code_bytes);
+    const rsrc_t vs = plane_rsrc(p.vs + (int64_t)kh * scale_bytes, scale_bytes);
+    half8_t *qlds = reinterpret_cast<half8_t *>(big);
+    const Offs sentinel{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
+
+    // first block of this pair: its loads go out before the Q prologue
+    int kb = pair;
+    const Offs lo = pair_lane_offsets<D>(w, g, n);
+    const uint32_t slot_unit = (uint32_t)(p.seq_base[b] + un.t0);
+    auto offs_for = [&](int blk) -> Offs {
+        return blk < nblk ? add_slot(lo, slot_unit + (uint32_t)(kBlockTokens * blk), D) : sentinel;
+    };
+    PairRaw<D> r;
+    {
+        const Offs o0 = offs_for(kb);
+        pair_load_k<D>(r, kc, ks, o0);
+        pair_load_v<D>(r, vc, vs, o0);
+    }
+    if (wave < NT) q_prologue<D>(p, b, kh, wave, lane, qlds, sm_c);
+    __syncthreads();
+    float cexp[NT];
+    int qi[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        const int row = 16 * rt + n;
+        cexp[rt] = sm_c[row];
+        qi[rt] = row < R ? row / G : p.n_q;          // padded rows see every key (their q is 0)
+    }
+
+    float4_t acc[NT][HT];    // rows 16 rt + 4 g + i, d = EPL n + HT w + t
+    float4_t lsum[NT];       // wave 0 of the pair: P . 1 over the same rows
+    float m[NT];             // pair-wide reference of row 16 rt + n (base 2)
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        m[rt] = -INFINITY;
+        lsum[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < HT; ++t) acc[rt][t] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
+
+    // offset limit of this pair's current block relative to L - n_q
+    int lim = (int)(un.L - p.n_q - un.t0) - kBlockTokens * kb;
+    const int iters = (nblk + kPairs - 1) / kPairs;
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" ::: "memory");     // Q fragments are re-read from LDS every block
+        const Offs on = offs_for(kb + kPairs);
+        // ---- S^T for this wave's 16 tokens
+        float4_t s[NT];
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) s[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const half8_t a = pair_dequant_k<D>(r, kk);
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+                s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlds[(rt * KK + kk) * 64 + lane], s[rt], 0, 0, 0);
+        }
+        pair_load_k<D>(r, kc, ks, on);
+        PairVPrep vp;
+        pair_v_prep<D>(vp, r);
+        __builtin_amdgcn_sched_barrier(0);
+        pair_load_v<D>(r, vc, vs, on);
+
+        // ---- scores; a pair past its last block masks everything (its data is zeros)
+        const int lim_eff = kb < nblk ? lim : -(1 << 30);
+        float x[NT][4], mloc[NT];
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[rt][i] = s[rt][i] * cexp[rt];
+        if (lim_eff < kBlockTokens - 1) {
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * w + 4 * g + i > lim_eff + qi[rt]) x[rt][i] = -INFINITY;
+        }
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            mloc[rt] = wave_max_g(fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3])));
+            if (g == 0) xmax[pair][w][16 * rt + n] = mloc[rt];
+        }
+        __syncthreads();                                   // 1: block maxima of both halves
+        bool need_any = false;
+        float mb[NT];
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            mb[rt] = fmaxf(mloc[rt], xmax[pair][1 - w][16 * rt + n]);
+            need_any |= mb[rt] > m[rt] + kLazyMax;
+        }
+        // both waves of the pair see the same maxima and m, so they decide alike
+        if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+                const bool need = mb[rt] > m[rt] + kLazyMax;
+                const float mnew = need ? mb[rt] : m[rt];
+                const float alpha = need ? exp2f(m[rt] - mnew) : 1.0f;   // m = -inf -> 0
+                m[rt] = mnew;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * g + i);       // accumulator row 4 g + i
+                    lsum[rt][i] *= ai;
+#pragma unroll
+                    for (int t = 0; t < HT; ++t) acc[rt][t][i] *= ai;
+                }
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const float mu = m[rt] == -INFINITY ? 0.0f : m[rt];
+            const half2_t p01 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][0] - mu),
+                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][1] - mu)};
+            const half2_t p23 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][2] - mu),
+                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][3] - mu)};
+            uint32_t *dst = reinterpret_cast<uint32_t *>(&pbuf[pair][rt][lane]) + 2 * w;
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{as_u32(p01), as_u32(p23)};
+        }
+        __syncthreads();                                   // 2: probabilities of both halves
+        half8_t pa[NT];
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) pa[rt] = __builtin_bit_cast(half8_t, pbuf[pair][rt][lane]);
+
+        // ---- O += P . V over this wave's half of head_dim
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+            uint32_t bw[4];
+#pragma unroll
+            for (int kp = 0; kp < 4; ++kp) {
+                const uint32_t src = (t & 1) ? vp.O[kp] : vp.E[kp];
+                uint32_t c;
+                switch (t >> 1) {
+                    case 0: c = fp4x2<0>(src); break;
+                    case 1: c = fp4x2<1>(src); break;
+                    case 2: c = fp4x2<2>(src); break;
+                    default: c = fp4x2<3>(src); break;
+                }
+                bw[kp] = hmul2(c, vp.SP[kp]);
+            }
+            const half8_t bh = __builtin_bit_cast(half8_t, u32x4_t{bw[0], bw[1], bw[2], bw[3]});
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+                acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], bh, acc[rt][t], 0, 0, 0);
+        }
+        if (w == 0) {
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+                lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], ones, lsum[rt], 0, 0, 0);
+        }
+        kb += kPairs;
+        lim -= (int)kPairStep;
+    }
+
+    // ---- merge the two pairs and write the unit's partial
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        if (w == 0 && g == 0) sm_m[pair][16 * rt + n] = m[rt];
+        if (w == 0 && n == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm_l[pair][16 * rt + 4 * g + i] = lsum[rt][i];
+        }
+    }
+    __syncthreads();                          // also ends every read of the Q fragments
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rt + 4 * g + i;
+            const float m0 = sm_m[0][row], m1 = sm_m[1][row];
+            const float M = fmaxf(m0, m1);
+            const float mp = pair ? m1 : m0;
+            const float f = mp == -INFINITY ? 0.0f : exp2f(mp - M);
+#pragma unroll
+            for (int t = 0; t < HT; ++t) acc[rt][t][i] *= f;
+        }
+    }
+    float4_t(*mbuf)[HT][64] = reinterpret_cast<float4_t(*)[HT][64]>(big);   // [role][t][lane]
+    float *ws_o = p.ws_o + (int64_t)u * R * D;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+        if (pair == 1) {
+#pragma unroll
+            for (int t = 0; t < HT; ++t) mbuf[w][t][lane] = acc[rt][t];
+        }
+        __syncthreads();
+        if (pair == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * rt + 4 * g + i;
+                if (row < R) {
+                    float *dst = ws_o + (int64_t)row * D + EPL * n + HT * w;
+#pragma unroll
+                    for (int t = 0; t < HT; t += 4)
+                        *reinterpret_cast<float4_t *>(dst + t) =
+                            float4_t{acc[rt][t][i] + mbuf[w][t][lane][i], acc[rt][t + 1][i] + mbuf[w][t + 1][lane][i],
+                                     acc[rt][t + 2][i] + mbuf[w][t + 2][lane][i],
+                                     acc[rt][t + 3][i] + mbuf[w][t + 3][lane][i]};
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x < R) {
+        const int row = threadIdx.x;
+        const float m0 = sm_m[0][row], m1 = sm_m[1][row];
+        const float M = fmaxf(m0, m1);
+        float Ls = 0.f;
+        if (m0 != -INFINITY) Ls += exp2f(m0 - M) * sm_l[0][row];
+        if (m1 != -INFINITY) Ls += exp2f(m1 - M) * sm_l[1][row];
+        p.ws_m[(int64_t)u * R + row] = M;
+        p.ws_l[(int64_t)u * R + row] = Ls;
+    }
+}
+
+template <int D, int NT>
+hipError_t launch_pair_t(const DecodeParams &p, hipStream_t s) {
+    hipLaunchKernelGGL((decode_pair_kernel<D, NT>), dim3(p.units), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_pair(const DecodeParams &p, int D, int NT, hipStream_t s) {
+    if (D == 256) {
+        switch (NT) {
+            case 2: return launch_pair_t<256, 2>(p, s);
+            case 3: return launch_pair_t<256, 3>(p, s);
+            case 4: return launch_pair_t<256, 4>(p, s);
+        }
+    } else if (D == 128) {
+        switch (NT) {
+            case 2: return launch_pair_t<128, 2>(p, s);
+            case 3: return launch_pair_t<128, 3>(p, s);
+            case 4: return launch_pair_t<128, 4>(p, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace nvfp4

@@ -13,6 +13,11 @@ constexpr int kBlockTokens = 32;     // tokens per KV block: one PV MFMA K-step 
 constexpr int kWaves = 4;            // waves per decode workgroup (256 threads)
 constexpr int kCUs = 256;            // compute units the split plan fills (MI355X)
 
+// Resident decode workgroups (256 threads) per CU that the partial kernel for NT row
+// tiles is built for: its waves per SIMD, set by its register budget. The split
+// planner fills that many per CU.
+constexpr int decode_wgs_per_cu(int NT) { return NT == 2 ? 3 : 2; }
+
 // Split-K plan: sequence b is cut into n_split[b] units of split_len[b] tokens
 // (a multiple of kBlockTokens; the last unit ends at the sequence length), for
 // each KV head. Units are numbered sequence-major, then KV head, then split.
@@ -63,7 +68,9 @@ struct CalibParams {
 
 hipError_t launch_calibrate(const CalibParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
+// NT == 1: four waves per block stream; NT 2..4: the wave-pair kernel.
 hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream_t s);
+hipError_t launch_decode_pair(const DecodeParams &p, int D, int NT, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeParams &p, int D, hipStream_t s);
 
 }  // namespace nvfp4

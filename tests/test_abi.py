@@ -70,6 +70,10 @@ def test_decode_validation_codes(lib):
     assert _call_decode(qk, lib, None) == qk.EINVAL
     assert "null" in lib.nvfp4_last_error().decode()
     assert _call_decode(qk, lib, _desc(qk, D=64)) == qk.EUNSUPPORTED
+    # one head's code plane must stay below 2^31 bytes (32-bit kernel offsets)
+    assert _call_decode(qk, lib, _desc(qk, cap=(2 ** 31 - 1) // 128 + 1)) == qk.EUNSUPPORTED
+    assert "capacity" in lib.nvfp4_last_error().decode()
+    assert _call_decode(qk, lib, _desc(qk, D=128, cap=(2 ** 31 - 1) // 64 + 1)) == qk.EUNSUPPORTED
     assert _call_decode(qk, lib, _desc(qk, H=0)) == qk.EINVAL
     assert _call_decode(qk, lib, _desc(qk, addr=0x100008)) == qk.EINVAL          # unaligned plane
     assert _call_decode(qk, lib, d, Hq=25) == qk.EUNSUPPORTED                      # Hq % Hkv
