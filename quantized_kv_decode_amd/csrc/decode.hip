@@ -312,7 +312,11 @@ void decode_partial_kernel(DecodeParams p) {
     const rsrc_t vs = plane_rsrc(p.vs + (int64_t)kh * scale_bytes, scale_bytes);
     half8_t *qlds = reinterpret_cast<half8_t *>(lds);
 
-    // The first block's loads go out before the Q prologue so both latencies overlap.
+    // Q row loads first, then the first block's KV loads: both latencies overlap, and the
+    // Q conversion waits only for Q (vector-memory waits are in order).
+    uint32_t qw[D / 8];
+    if (wave < NT) q_load<D>(p, b, kh, wave, lane, qw);
+    __builtin_amdgcn_sched_barrier(0);
     Raw<D> r;
     int kb = wave;
     Offs o = lane_offsets<D>(base + t0 + (int64_t)kBlockTokens * kb, g, n);
@@ -324,7 +328,7 @@ void decode_partial_kernel(DecodeParams p) {
     }
 
     // ---- Q rows -> fp16 fragments in LDS (wave rt converts row tile rt)
-    if (wave < NT) q_prologue<D>(p, b, kh, wave, lane, qlds, sm_c);
+    if (wave < NT) q_store<D>(p, b, kh, wave, lane, qw, qlds, sm_c);
     __syncthreads();
     float cexp[NT];
     int qi[NT];
@@ -405,24 +409,33 @@ void decode_partial_kernel(DecodeParams p) {
     float *ws_o = p.ws_o + (int64_t)u * R * D;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
+        // Only rows below R are stored. Lane n's D/16 values sit at a stride of D/16 floats
+        // from lane n + 1's, so lanes n, n + 2, ... share LDS banks; rotating the order of the
+        // 4-float chunks by n / 2 spreads them over the banks.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float *dst = &buf[wave][4 * g + i][EPL * n];
+            if (16 * rt + 4 * g + i < R) {
+                float *dst = &buf[wave][4 * g + i][EPL * n];
 #pragma unroll
-            for (int dt = 0; dt < EPL; dt += 4)
-                *reinterpret_cast<float4_t *>(dst + dt) =
-                    float4_t{st.acc[rt][dt][i], st.acc[rt][dt + 1][i], st.acc[rt][dt + 2][i], st.acc[rt][dt + 3][i]};
+                for (int c = 0; c < EPL / 4; ++c) {
+                    const int dt = 4 * ((c + (n >> 1)) & (EPL / 4 - 1));
+                    float4_t v;
+#pragma unroll
+                    for (int k = 0; k < EPL / 4; ++k)      // select chunk dt without dynamic indexing
+                        if (4 * k == dt) v = float4_t{st.acc[rt][4 * k][i], st.acc[rt][4 * k + 1][i],
+                                                      st.acc[rt][4 * k + 2][i], st.acc[rt][4 * k + 3][i]};
+                    *reinterpret_cast<float4_t *>(dst + dt) = v;
+                }
+            }
         }
         __syncthreads();
-        for (int e = threadIdx.x; e < 16 * D; e += 256) {
+        const int rows = min(16, R - 16 * rt);
+        for (int e = threadIdx.x; e < rows * D; e += 256) {
             const int r16 = e / D, d = e - r16 * D;
-            const int row = 16 * rt + r16;
-            if (row < R) {
-                float sum = 0.f;
+            float sum = 0.f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) sum += buf[w][r16][d];
-                ws_o[(int64_t)row * D + d] = sum;
-            }
+            for (int w = 0; w < kWaves; ++w) sum += buf[w][r16][d];
+            ws_o[(int64_t)(16 * rt + r16) * D + d] = sum;
         }
         __syncthreads();
     }
@@ -465,7 +478,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     vecf acc = {};
     float den = 0.f;
     const float *orow = p.ws_o + (u0 * R + r) * D + PER * lane;
-#pragma unroll 4
+    // all of a wave's loads in flight together (one memory latency, not one per unit)
+#pragma unroll 16
     for (int s = wave; s < ns; s += kWaves) {
         const float ms = mrow[(int64_t)s * R];
         const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);

@@ -88,22 +88,21 @@ __device__ inline Unit unit_of(const DecodeParams &p, int u) {
     return r;
 }
 
-// Query rows of row tile rt -> fp16 MFMA B-fragments in LDS, run by one wave.
+// Query rows of row tile rt -> fp16 MFMA B-fragments in LDS, run by one wave in two
+// steps: q_load issues the row loads (before the first KV block's loads, so waiting for
+// Q does not wait for KV), q_store converts and stores.
 // Fragment (rt, kk, lane (g, n)) = row 16 rt + n, d in [D/4 g + 8 kk, D/4 g + 8 kk + 8).
 // Each row is scaled by an exact power of two that brings its maximum magnitude to
 // [2^14, 2^15) before the fp16 conversion; sm_c[row] receives the factor that turns an
 // MFMA score back into sm_scale * q . k_hat * log2(e) (including the 2^8 of the
 // dequantised K and g_K). Rows past R get zero fragments and factor 0.
 template <int D>
-__device__ inline void q_prologue(const DecodeParams &p, int b, int kh, int rt, int lane, half8_t *qlds,
-                                  float *sm_c) {
+__device__ inline void q_load(const DecodeParams &p, int b, int kh, int rt, int lane, uint32_t (&w)[D / 8]) {
     constexpr int KK = D / 32;
     constexpr int QD = D / 4;
     const int n = lane & 15, g = lane >> 4;
     const int row = 16 * rt + n;
-    const bool valid = row < p.R;
-    uint32_t w[KK * 4];
-    if (valid) {
+    if (row < p.R) {
         const int i = row / p.G;
         const int h = kh * p.G + (row - i * p.G);
         const uint16_t *qr = p.q + (((int64_t)b * p.n_q + i) * p.Hq + h) * D + QD * g;
@@ -116,6 +115,14 @@ __device__ inline void q_prologue(const DecodeParams &p, int b, int kh, int rt, 
 #pragma unroll
         for (int k = 0; k < KK * 4; ++k) w[k] = 0u;
     }
+}
+
+template <int D>
+__device__ inline void q_store(const DecodeParams &p, int b, int kh, int rt, int lane, const uint32_t (&w)[D / 8],
+                               half8_t *qlds, float *sm_c) {
+    constexpr int KK = D / 32;
+    const int n = lane & 15, g = lane >> 4;
+    const int row = 16 * rt + n;
     uint32_t am = 0;
 #pragma unroll
     for (int k = 0; k < KK * 4; ++k) am = max(am, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
@@ -138,7 +145,7 @@ __device__ inline void q_prologue(const DecodeParams &p, int b, int kh, int rt, 
     }
     if (g == 0) {
         const float gk = p.gscale[(b * p.Hkv + kh) * 2 + 0];
-        sm_c[row] = valid ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
+        sm_c[row] = row < p.R ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
     }
 }
 

@@ -142,7 +142,7 @@ void decode_pair_kernel(DecodeParams p) {
     using LD = PairLds<D, NT>;
     __shared__ __attribute__((aligned(16))) uint8_t big[LD::BIG];
     __shared__ __attribute__((aligned(16))) u32x4_t pbuf[kPairs][NT][64];   // (mt 0 | mt 1) fp16 P per lane
-    __shared__ float xmax[kPairs][2][NT * 16];
+    __shared__ float xmax[kPairs][2][2][NT * 16];                         // [pair][parity][half]
     __shared__ float sm_c[kMaxRows];
     __shared__ float sm_m[kPairs][kMaxRows];
     __shared__ float sm_l[kPairs][kMaxRows];
@@ -162,7 +162,11 @@ void decode_pair_kernel(DecodeParams p) {
     half8_t *qlds = reinterpret_cast<half8_t *>(big);
     const Offs sentinel{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
 
-    // first block of this pair: its loads go out before the Q prologue
+    // Q row loads first, then the pair's first block: both latencies overlap, and the Q
+    // conversion waits only for Q (vector-memory waits are in order).
+    uint32_t qw[D / 8];
+    if (wave < NT) q_load<D>(p, b, kh, wave, lane, qw);
+    __builtin_amdgcn_sched_barrier(0);
     int kb = pair;
     const Offs lo = pair_lane_offsets<D>(w, g, n);
     const uint32_t slot_unit = (uint32_t)(p.seq_base[b] + un.t0);
@@ -175,7 +179,7 @@ void decode_pair_kernel(DecodeParams p) {
         pair_load_k<D>(r, kc, ks, o0);
         pair_load_v<D>(r, vc, vs, o0);
     }
-    if (wave < NT) q_prologue<D>(p, b, kh, wave, lane, qlds, sm_c);
+    if (wave < NT) q_store<D>(p, b, kh, wave, lane, qw, qlds, sm_c);
     __syncthreads();
     float cexp[NT];
     int qi[NT];
@@ -198,13 +202,23 @@ void decode_pair_kernel(DecodeParams p) {
     }
     const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
 
-    // offset limit of this pair's current block relative to L - n_q
-    int lim = (int)(un.L - p.n_q - un.t0) - kBlockTokens * kb;
+    // The pair's j-th block is block pair + 2 j of the unit. One loop trip finishes block j
+    // and starts block j + 1, so the softmax chain and the barrier waits of block j overlap
+    // the dequantisation and MFMAs of block j + 1:
+    //   barrier A  -> partner's row maxima of block j -> reference m, P(j) to LDS;
+    //                 V(j) interleave, V(j + 1) loads; S^T(j + 1), K(j + 2) loads,
+    //                 scores and row maxima of block j + 1 to LDS (other parity)
+    //   barrier B  -> P(j) of both halves -> O += P(j) . V(j)
+    // lim: offset limit of the block relative to L - n_q (32-bit: tokens < 2^31).
+    const int lim0 = (int)(un.L - p.n_q - un.t0) - kBlockTokens * pair;
     const int iters = (nblk + kPairs - 1) / kPairs;
-    for (int it = 0; it < iters; ++it) {
+    float x[NT][4], mloc[NT];
+
+    // S^T of the pair's block j from the K words in r, the K loads of block j + 1, and
+    // the block's masked scores and row maxima (published in xmax[j & 1]). A block past
+    // the pair's last one masks everything (its words are zeros).
+    auto start_block = [&](int j) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");     // Q fragments are re-read from LDS every block
-        const Offs on = offs_for(kb + kPairs);
-        // ---- S^T for this wave's 16 tokens
         float4_t s[NT];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) s[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -215,37 +229,34 @@ void decode_pair_kernel(DecodeParams p) {
             for (int rt = 0; rt < NT; ++rt)
                 s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlds[(rt * KK + kk) * 64 + lane], s[rt], 0, 0, 0);
         }
-        pair_load_k<D>(r, kc, ks, on);
-        PairVPrep vp;
-        pair_v_prep<D>(vp, r);
-        __builtin_amdgcn_sched_barrier(0);
-        pair_load_v<D>(r, vc, vs, on);
-
-        // ---- scores; a pair past its last block masks everything (its data is zeros)
-        const int lim_eff = kb < nblk ? lim : -(1 << 30);
-        float x[NT][4], mloc[NT];
+        pair_load_k<D>(r, kc, ks, offs_for(pair + kPairs * (j + 1)));
+        const int lim = pair + kPairs * j < nblk ? lim0 - (int)kPairStep * j : -(1 << 30);
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[rt][i] = s[rt][i] * cexp[rt];
-        if (lim_eff < kBlockTokens - 1) {
+        if (lim < kBlockTokens - 1) {
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (16 * w + 4 * g + i > lim_eff + qi[rt]) x[rt][i] = -INFINITY;
+                    if (16 * w + 4 * g + i > lim + qi[rt]) x[rt][i] = -INFINITY;
         }
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             mloc[rt] = wave_max_g(fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3])));
-            if (g == 0) xmax[pair][w][16 * rt + n] = mloc[rt];
+            if (g == 0) xmax[pair][j & 1][w][16 * rt + n] = mloc[rt];
         }
-        __syncthreads();                                   // 1: block maxima of both halves
+    };
+
+    start_block(0);
+    for (int j = 0; j < iters; ++j) {
+        __syncthreads();                                   // A: row maxima of block j
         bool need_any = false;
         float mb[NT];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
-            mb[rt] = fmaxf(mloc[rt], xmax[pair][1 - w][16 * rt + n]);
+            mb[rt] = fmaxf(mloc[rt], xmax[pair][j & 1][1 - w][16 * rt + n]);
             need_any |= mb[rt] > m[rt] + kLazyMax;
         }
         // both waves of the pair see the same maxima and m, so they decide alike
@@ -276,12 +287,17 @@ void decode_pair_kernel(DecodeParams p) {
             typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
             *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{as_u32(p01), as_u32(p23)};
         }
-        __syncthreads();                                   // 2: probabilities of both halves
+        PairVPrep vp;
+        pair_v_prep<D>(vp, r);
+        __builtin_amdgcn_sched_barrier(0);
+        pair_load_v<D>(r, vc, vs, offs_for(pair + kPairs * (j + 1)));
+        if (j + 1 < iters) start_block(j + 1);
+        __syncthreads();                                   // B: probabilities of block j
         half8_t pa[NT];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) pa[rt] = __builtin_bit_cast(half8_t, pbuf[pair][rt][lane]);
 
-        // ---- O += P . V over this wave's half of head_dim
+        // ---- O += P(j) . V(j) over this wave's half of head_dim
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
             uint32_t bw[4];
@@ -307,8 +323,6 @@ void decode_pair_kernel(DecodeParams p) {
             for (int rt = 0; rt < NT; ++rt)
                 lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], ones, lsum[rt], 0, 0, 0);
         }
-        kb += kPairs;
-        lim -= (int)kPairStep;
     }
 
     // ---- merge the two pairs and write the unit's partial
