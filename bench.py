@@ -170,11 +170,13 @@ def main() -> int:
     def k_combine(p):
         qk.decode_attn_combine(p, g, out, seq_lens, ws)
 
+    def k_decode_step(p):
+        # one decode step: the decode kernel stores the step's n_q rows per sequence itself
+        # (fused append), then the combine kernel: two launches
+        qk.decode_step(p, g, k_step, v_step, q, w.seq_base, seq_lens, w.sm_scale, out=out, workspace=ws)
+
     def step(i):
-        p = pools[i % R]
-        k_append(p)
-        k_partial(p)
-        k_combine(p)
+        k_decode_step(pools[i % R])
 
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb << 20
@@ -215,7 +217,7 @@ def main() -> int:
         e1.synchronize()
         return e0.elapsed_time(e1)                            # ms
 
-    g_step = capture([k_append, k_partial, k_combine], K)
+    g_step = capture([k_decode_step], K)
     g_part = capture([k_partial], K)
     g_comb = capture([k_combine], K)
     g_app = capture([k_append], K)
@@ -272,7 +274,7 @@ def main() -> int:
             "kv_bytes_per_step": kv,
             "rotation_copies": R,
             "timing": "one HIP-graph replay of K steps between events",
-            "step": "append n_q rows/seq + split-K partial + combine",
+            "step": "decode step (nvfp4_decode_step): split-K partial with the n_q-row append fused in, then combine",
         },
         "kernels_us": {"append": round(ms_app * 1e3, 3), "decode_partial": round(ms_part * 1e3, 3),
                        "decode_combine": round(ms_comb * 1e3, 3)},

@@ -131,6 +131,26 @@ int nvfp4_decode_attn(const nvfp4_kv_cache *cache, const float *global_scale, co
                       const int64_t *seq_len, int32_t n_q, int32_t num_q_heads, float sm_scale,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* One decode step of the batch (knoopx/ninfer page, "Capabilities and limits": batched
+ * decode of one to eight requests and MTP verification of one to five drafts, run as
+ * exact-batch graphs): stores the step's n_q new K/V rows of every sequence, then
+ * attends over the whole sequence. Equivalent to
+ *   nvfp4_kv_append(cache, k_new, v_new, global_scale, num_seqs, seq_base,
+ *                   write_pos = seq_len - n_q, n_new = n_q, stream)
+ * followed by nvfp4_decode_attn(...) with the same arguments, and bit-identical to
+ * that pair (pool bytes and out); the rows are quantised inside the decode kernel by
+ * the workgroups that read them, so the step is two kernel launches instead of three.
+ *   k_new, v_new: device bf16 [num_seqs * n_q][num_kv_heads][head_dim], sequence 0's
+ *                 n_q rows first; row r of sequence b goes to slot
+ *                 seq_base[b] + seq_len[b] - n_q + r.
+ *   Other arguments, the workspace and the errors as for nvfp4_decode_attn (EINVAL
+ *   also for null or unaligned k_new / v_new). */
+int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, const void *k_new,
+                      const void *v_new, const void *q, void *out, int32_t out_dtype,
+                      int32_t num_seqs, const int64_t *seq_base, const int64_t *seq_len,
+                      int32_t n_q, int32_t num_q_heads, float sm_scale, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* The two kernels of nvfp4_decode_attn, callable on their own (same arguments,
  * same workspace) so that each can be timed: the split-K partial pass writes
  * per-split (o, m, l) into the workspace; the combine pass merges them by

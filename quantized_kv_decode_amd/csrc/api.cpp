@@ -116,7 +116,10 @@ int make_plan(const nvfp4_kv_cache *c, int32_t num_seqs, const int64_t *seq_base
     for (int b = 0; b < num_seqs; ++b) {
         int64_t len = (seq_len[b] + nsp[b] - 1) / nsp[b];
         len = (len + nvfp4::kBlockTokens - 1) / nvfp4::kBlockTokens * nvfp4::kBlockTokens;
-        const int64_t ns = (seq_len[b] + len - 1) / len;
+        int64_t ns = (seq_len[b] + len - 1) / len;
+        // The last unit must hold the n_q newest tokens (a decode step appends them in
+        // the workgroup that reads them): a shorter remainder joins the unit before it.
+        if (ns > 1 && seq_len[b] - (ns - 1) * len < n_q) ns -= 1;
         pl.split_len[b] = (int32_t)len;
         pl.n_split[b] = (int32_t)ns;
         pl.unit_base[b] = ub;
@@ -142,10 +145,10 @@ void fill_decode(nvfp4::DecodeParams &dp, const nvfp4::SplitPlan &pl, const nvfp
                  const float *global_scale, const void *q, const int64_t *seq_base, const int64_t *seq_len,
                  float sm_scale, void *workspace) {
     std::memset(&dp, 0, sizeof dp);
-    dp.kc = static_cast<const uint8_t *>(c->k_codes);
-    dp.ks = static_cast<const uint8_t *>(c->k_scales);
-    dp.vc = static_cast<const uint8_t *>(c->v_codes);
-    dp.vs = static_cast<const uint8_t *>(c->v_scales);
+    dp.kc = static_cast<uint8_t *>(c->k_codes);
+    dp.ks = static_cast<uint8_t *>(c->k_scales);
+    dp.vc = static_cast<uint8_t *>(c->v_codes);
+    dp.vs = static_cast<uint8_t *>(c->v_scales);
     dp.cap = c->capacity;
     dp.gscale = global_scale;
     dp.q = static_cast<const uint16_t *>(q);
@@ -296,6 +299,35 @@ int nvfp4_decode_attn_combine(const nvfp4_kv_cache *cache, const float *global_s
     dp.out_bf16 = out_dtype == NVFP4_OUT_BF16;
     return hip_status(nvfp4::launch_decode_combine(dp, pl.D, static_cast<hipStream_t>(stream)),
                       "decode combine launch");
+}
+
+int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, const void *k_new,
+                      const void *v_new, const void *q, void *out, int32_t out_dtype, int32_t num_seqs,
+                      const int64_t *seq_base, const int64_t *seq_len, int32_t n_q, int32_t num_q_heads,
+                      float sm_scale, void *workspace, size_t workspace_bytes, void *stream) {
+    // Validate everything before the first launch so a failed call enqueues nothing.
+    nvfp4::SplitPlan pl;
+    if (!seq_base) return fail(NVFP4_EINVAL, "seq_base is null");
+    int rc = make_plan(cache, num_seqs, seq_base, seq_len, n_q, num_q_heads, pl);
+    if (rc) return rc;
+    if ((rc = check_decode_common(global_scale, workspace, workspace_bytes, pl))) return rc;
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return fail(NVFP4_EINVAL, "k_new and v_new must be non-null and 16-byte aligned");
+    if (!aligned16(q)) return fail(NVFP4_EINVAL, "q must be non-null and 16-byte aligned");
+    if (!aligned16(out)) return fail(NVFP4_EINVAL, "out must be non-null and 16-byte aligned");
+    if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16)
+        return fail(NVFP4_EINVAL, "out_dtype %d invalid", out_dtype);
+    if (!std::isfinite(sm_scale)) return fail(NVFP4_EINVAL, "sm_scale must be finite");
+    nvfp4::DecodeParams dp;
+    fill_decode(dp, pl, cache, global_scale, q, seq_base, seq_len, sm_scale, workspace);
+    dp.k_new = static_cast<const uint16_t *>(k_new);
+    dp.v_new = static_cast<const uint16_t *>(v_new);
+    dp.out = out;
+    dp.out_bf16 = out_dtype == NVFP4_OUT_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = nvfp4::launch_decode_partial(dp, pl.D, pl.NT, s);
+    if (e != hipSuccess) return hip_status(e, "decode partial launch");
+    return hip_status(nvfp4::launch_decode_combine(dp, pl.D, s), "decode combine launch");
 }
 
 int nvfp4_decode_attn(const nvfp4_kv_cache *cache, const float *global_scale, const void *q, void *out,

@@ -7,6 +7,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "quantize.h"
 
 namespace nvfp4 {
 namespace dev {
@@ -66,9 +67,10 @@ struct Offs {
 constexpr uint32_t kPastPlane = 0x80000000u;
 
 // Unit u of the split plan: sequence b, KV head kh, tokens [t0, t1) of the
-// sequence (length L), nblk 32-token blocks.
+// sequence (length L), nblk 32-token blocks; last: the unit ending at L.
 struct Unit {
     int b, kh, nblk;
+    bool last;
     int64_t L, t0, t1;
 };
 
@@ -82,10 +84,37 @@ __device__ inline Unit unit_of(const DecodeParams &p, int u) {
     r.kh = local / p.n_split[r.b];
     const int sp = local - r.kh * p.n_split[r.b];
     r.L = p.seq_len[r.b];
+    r.last = sp == p.n_split[r.b] - 1;
     r.t0 = (int64_t)sp * p.split_len[r.b];
-    r.t1 = min(r.t0 + (int64_t)p.split_len[r.b], r.L);
+    r.t1 = r.last ? r.L : r.t0 + p.split_len[r.b];
     r.nblk = (int)((r.t1 - r.t0 + kBlockTokens - 1) / kBlockTokens);
     return r;
+}
+
+// The n_q rows a decode step appends for (sequence b, KV head kh) before reading
+// them: rows b n_q + r (r < n_q) of k_new / v_new, quantised with the sequence's
+// global scales by the append kernel's group quantiser and stored at slots
+// seq_base[b] + L - n_q + r. One thread per (K|V, row, group of 16). The caller
+// fences before any of its loads can touch those slots.
+template <int D>
+__device__ inline void append_step_rows(const DecodeParams &p, int b, int kh, int64_t L) {
+    constexpr int groups = D / 16;
+    const int per_kv = p.n_q * groups;
+    for (int t = threadIdx.x; t < 2 * per_kv; t += blockDim.x) {
+        const int kv = t >= per_kv;                   // 0 = K, 1 = V
+        const int rem = t - kv * per_kv;
+        const int r = rem / groups, j = rem - r * groups;
+        const int64_t row = (int64_t)b * p.n_q + r;
+        const uint16_t *src = (kv ? p.v_new : p.k_new) + (row * p.Hkv + kh) * D + 16 * j;
+        const uint4 w0 = *reinterpret_cast<const uint4 *>(src);
+        const uint4 w1 = *reinterpret_cast<const uint4 *>(src + 8);
+        const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        uint32_t packed[2];
+        const uint32_t sc = quantize_group(w, (double)p.gscale[(b * p.Hkv + kh) * 2 + kv], packed);
+        const int64_t plane_row = (int64_t)kh * p.cap + p.seq_base[b] + L - p.n_q + r;
+        *reinterpret_cast<uint2 *>((kv ? p.vc : p.kc) + plane_row * (D / 2) + 8 * j) = make_uint2(packed[0], packed[1]);
+        (kv ? p.vs : p.ks)[plane_row * groups + j] = (uint8_t)sc;
+    }
 }
 
 // Query rows of row tile rt -> fp16 MFMA B-fragments in LDS, run by one wave in two

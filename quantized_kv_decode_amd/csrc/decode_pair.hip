@@ -166,6 +166,14 @@ void decode_pair_kernel(DecodeParams p) {
     // conversion waits only for Q (vector-memory waits are in order).
     uint32_t qw[D / 8];
     if (wave < NT) q_load<D>(p, b, kh, wave, lane, qw);
+    // A decode step that appends its own rows: the workgroup of the sequence's last unit
+    // (the only one that reads those slots) stores them before issuing any KV load. The
+    // workgroup barrier orders the stores before every wave's later loads (workgroup-scope
+    // visibility of global memory: all waves share this CU's vector cache).
+    if (p.k_new != nullptr && un.last) {
+        append_step_rows<D>(p, b, kh, un.L);
+        __syncthreads();
+    }
     __builtin_amdgcn_sched_barrier(0);
     int kb = pair;
     const Offs lo = pair_lane_offsets<D>(w, g, n);

@@ -19,8 +19,10 @@ constexpr int kCUs = 256;            // compute units the split plan fills (MI35
 constexpr int decode_wgs_per_cu(int NT) { return NT == 2 ? 3 : 2; }
 
 // Split-K plan: sequence b is cut into n_split[b] units of split_len[b] tokens
-// (a multiple of kBlockTokens; the last unit ends at the sequence length), for
-// each KV head. Units are numbered sequence-major, then KV head, then split.
+// (a multiple of kBlockTokens) for each KV head; the last unit ends at the
+// sequence length and holds at least n_q tokens (so the rows a decode step
+// appends all fall in it). Units are numbered sequence-major, then KV head, then
+// split.
 struct SplitPlan {
     int32_t B, Hkv, Hq, G, n_q, R, NT, D;
     int32_t n_split[kMaxSeqs];
@@ -31,10 +33,11 @@ struct SplitPlan {
 
 // Kernel parameters of the decode pair (passed by value).
 struct DecodeParams {
-    const uint8_t *kc, *ks, *vc, *vs;   // pool planes
+    uint8_t *kc, *ks, *vc, *vs;          // pool planes (written only by the step's own append)
     int64_t cap;
     const float *gscale;                 // [B][Hkv][2]
     const uint16_t *q;                   // bf16 [B][n_q][Hq][D]
+    const uint16_t *k_new, *v_new;       // bf16 [B n_q][Hkv][D] rows to append first, or null
     float *ws_o, *ws_m, *ws_l;           // [units][R][D], [units][R], [units][R]
     void *out;
     int32_t out_bf16;

@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn_workspace_bytes", "nvfp4_decode_attn",
-              "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine", "nvfp4_last_error"):
+              "nvfp4_decode_step", "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine", "nvfp4_last_error"):
         assert f in names
 
 
@@ -127,3 +127,37 @@ def test_workspace_query(lib):
     assert small >= 4 * 6 * (256 + 2) * 4
     # a long sequence is cut into at most two workgroups per CU for one row tile
     assert big <= 2 * 256 * 6 * (256 + 2) * 4 + 3 * 256
+
+
+def test_decode_step_validation_codes(lib):
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk)
+    a = 0x600000
+
+    def call(k=a, v=a, q=0x200000, out=0x300000, lens=(100,), base=(0,), n_q=1, ws=1 << 30):
+        return lib.nvfp4_decode_step(ctypes.byref(d), 0x400000, k, v, q, out, 0, 1, qk._i64(base), qk._i64(lens),
+                                     n_q, 24, 0.0625, 0x500000, ws, None)
+    assert call(k=0) == qk.EINVAL
+    assert call(v=a + 8) == qk.EINVAL
+    assert call(q=0) == qk.EINVAL
+    assert call(lens=(0,)) == qk.ERANGE
+    assert call(base=(950,)) == qk.ERANGE
+    assert call(ws=16) == qk.EWORKSPACE
+
+
+def test_split_plan_last_unit_holds_new_rows(lib):
+    """A decode step appends its n_q rows in the workgroup of the sequence's last unit, so
+    a remainder shorter than n_q joins the unit before it. L = 4003 at 4 KV heads is cut
+    into units of 160 tokens (31 wanted, at least 128 tokens each): 25 full units and a
+    3-token remainder. The workspace size (units x R x (D + 2) floats, parts 256-byte
+    aligned) shows the unit count."""
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk, cap=10 ** 6)
+    al = lambda x: (x + 255) // 256 * 256
+
+    def expected(units, R, D=256):
+        return al(units * R * D * 4) + 2 * al(units * R * 4)
+    ws = lambda L, n_q: lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([L]), n_q, 24)
+    assert ws(4003, 3) == expected(26 * 4, 6 * 3)        # remainder 3 >= n_q: its own unit
+    assert ws(4003, 4) == expected(25 * 4, 6 * 4)        # remainder 3 < n_q: merged
+    assert ws(4003, 6) == expected(25 * 4, 6 * 6)

@@ -179,6 +179,44 @@ def test_decode_matches_oracle(qk, shape):
     assert torch.equal(outb, out.to(torch.bfloat16))
 
 
+STEP_SHAPES = DECODE_SHAPES + [
+    dict(seq_lens=(4003,), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=6),      # 3-token remainder joins
+    dict(seq_lens=(4003, 161, 4), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=4),
+]
+
+
+@pytest.mark.parametrize("shape", STEP_SHAPES)
+def test_decode_step_equals_append_then_decode(qk, shape):
+    """The fused step, where the decode kernel stores the step's n_q rows itself, leaves
+    the same pool bytes and writes the same output bits as nvfp4_kv_append followed by
+    nvfp4_decode_attn, and both match the oracle."""
+    w = workloads.small(**shape)
+    say("decode step", shape)
+    ref = OracleRun(w)
+    kd, vd = ref.k.cuda(), ref.v.cuda()
+    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device="cuda")
+    g = qk.calibrate(pool, kd, vd, list(w.seq_lens))
+    pre = [L - w.n_q for L in w.seq_lens]
+    sl = lambda t, lo, hi: torch.cat([t[w.seq_base[b] + lo[b]:w.seq_base[b] + hi[b]] for b in range(w.batch)])
+    qk.append(pool, sl(kd, [0] * w.batch, pre).contiguous(), sl(vd, [0] * w.batch, pre).contiguous(), g,
+              w.seq_base, [0] * w.batch, pre)
+    k_step = sl(kd, pre, list(w.seq_lens)).contiguous()
+    v_step = sl(vd, pre, list(w.seq_lens)).contiguous()
+    copy = lambda p: qk.KVPool.from_planes(p.k_codes.clone(), p.k_scales.clone(), p.v_codes.clone(),
+                                           p.v_scales.clone())
+    pool_a, pool_b = copy(pool), copy(pool)
+    q = ref.q.cuda()
+    qk.append(pool_a, k_step, v_step, g, w.seq_base, pre, [w.n_q] * w.batch)
+    out_a = qk.decode_attn(pool_a, g, q, w.seq_base, list(w.seq_lens), w.sm_scale)
+    out_b = qk.decode_step(pool_b, g, k_step, v_step, q, w.seq_base, list(w.seq_lens), w.sm_scale)
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        assert torch.equal(getattr(pool_a, name), getattr(pool_b, name)), name
+    assert torch.equal(out_a, out_b)
+    assert_planes_equal(pool_b, ref.cache)
+    _check_decode(w, ref, out_b)
+
+
 def test_decode_deterministic_and_partial_combine_split(qk):
     w = workloads.small(seq_lens=(5000, 1234), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=6)
     say("determinism")
