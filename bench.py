@@ -37,9 +37,13 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+# Sources that shape the partial kernel's memory traffic (kernels, shared device code, planner).
+DIGEST_SOURCES = ("decode.hip", "decode_pair.hip", "decode_common.h", "quantize.h", "internal.h", "api.cpp")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip", "internal.h"):
+    for f in DIGEST_SOURCES:
         h.update(open(os.path.join(ROOT, "quantized_kv_decode_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
