@@ -462,14 +462,16 @@ void decode_partial_kernel(DecodeParams p) {
 }
 
 // One 256-thread workgroup per (sequence, KV head, row). Wave w merges units
-// w, w + 4, ... of that (sequence, head); lane c owns the D/64 contiguous outputs
-// [c D/64, (c + 1) D/64). The four wave results are merged through LDS. Every sum
-// runs in a fixed order, so the result does not depend on timing.
+// w, w + 4, ... of that (sequence, head) with its own running maximum (m, l and o of
+// a unit are loaded together, so the merge costs one memory latency, not two); lane c
+// owns the D/64 contiguous outputs [c D/64, (c + 1) D/64). The four wave results are
+// merged through LDS. Every sum runs in a fixed order, so the result does not depend
+// on timing.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     constexpr int PER = D / 64;                       // outputs per lane
     typedef float vecf __attribute__((ext_vector_type(PER)));
-    const int R = p.R, G = p.G;
+    const int R = p.R;
     const int blk = blockIdx.x;
     const int r = blk % R;
     const int bk = blk / R;
@@ -479,34 +481,62 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const float *mrow = p.ws_m + u0 * R + r;          // m of unit s at mrow[s * R]
     const float *lrow = p.ws_l + u0 * R + r;
-    float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, mrow[(int64_t)s * R]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    vecf acc = {};
-    float den = 0.f;
     const float *orow = p.ws_o + (u0 * R + r) * D + PER * lane;
-    // all of a wave's loads in flight together (one memory latency, not one per unit)
-#pragma unroll 16
-    for (int s = wave; s < ns; s += kWaves) {
-        const float ms = mrow[(int64_t)s * R];
-        const float w = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-        const vecf o = *reinterpret_cast<const vecf *>(orow + (int64_t)s * R * D);
-        acc += w * o;
-        den += w * lrow[(int64_t)s * R];
+    // batches of 8 units: every load of a batch is issued before any of it is used
+    constexpr int BATCH = 8;
+    // m and l are the same for every lane; an index the compiler cannot prove uniform
+    // keeps their loads on the vector path, where a batch's loads go out together (as
+    // scalar loads they were issued one after another)
+    int vz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+    float M = -INFINITY, den = 0.f;
+    vecf acc = {};
+    for (int s0 = wave; s0 < ns; s0 += kWaves * BATCH) {
+        float ms[BATCH], ls[BATCH];
+        vecf o[BATCH];
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const int s = s0 + k * kWaves;
+            const int64_t sc = s < ns ? s : ns - 1;      // past the end: a real unit, weight 0
+            ms[k] = mrow[sc * R + vz];
+            ls[k] = lrow[sc * R + vz];
+            o[k] = *reinterpret_cast<const vecf *>(orow + sc * R * D);
+            if (s >= ns) ms[k] = -INFINITY;
+        }
+        float mb = ms[0];
+#pragma unroll
+        for (int k = 1; k < BATCH; ++k) mb = fmaxf(mb, ms[k]);
+        const float Mn = fmaxf(M, mb);
+        const float f = M == -INFINITY ? 0.0f : exp2f(M - Mn);
+        acc *= f;
+        den *= f;
+        M = Mn;
+#pragma unroll
+        for (int k = 0; k < BATCH; ++k) {
+            const float w = ms[k] == -INFINITY ? 0.0f : exp2f(ms[k] - M);
+            acc += w * o[k];
+            den += w * ls[k];
+        }
     }
     __shared__ vecf part[kWaves][64];
-    __shared__ float dpart[kWaves];
+    __shared__ float mpart[kWaves], dpart[kWaves];
     part[wave][lane] = acc;
-    if (lane == 0) dpart[wave] = den;
+    if (lane == 0) {
+        mpart[wave] = M;
+        dpart[wave] = den;
+    }
     __syncthreads();
     if (wave == 0) {
-        vecf o = part[0][lane];
-        float dd = dpart[0];
+        float Mx = mpart[0];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            o += part[w][lane];
-            dd += dpart[w];
+        for (int w = 1; w < kWaves; ++w) Mx = fmaxf(Mx, mpart[w]);
+        vecf o = {};
+        float dd = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = mpart[w] == -INFINITY ? 0.0f : exp2f(mpart[w] - Mx);
+            o += f * part[w][lane];
+            dd += f * dpart[w];
         }
         // v_hat = (e2m1 * S * 2^-8) * 2^8 * g_V
         o *= 256.0f * p.gscale[(b * p.Hkv + kh) * 2 + 1] / dd;
