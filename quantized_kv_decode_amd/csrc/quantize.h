@@ -83,12 +83,19 @@ __device__ inline uint32_t thr_ge(double T) {
     return f32_bits(nextafterf(u, 0.0f)) >> 16;     // u > 0 here
 }
 
-// Magnitude code of a bf16 magnitude a16 given the group's seven thresholds:
-// u[k] <-> midpoint k in (0.25 >, 0.75 >=, 1.25 >, 1.75 >=, 2.5 >, 3.5 >=, 5 >).
-__device__ inline uint32_t e2m1_mag(uint32_t a16, const uint32_t u[7]) {
-    const uint32_t c1 = a16 > u[3];
-    const uint32_t c2 = a16 > (c1 ? u[5] : u[1]);
-    const uint32_t t3 = c1 ? (c2 ? u[6] : u[4]) : (c2 ? u[2] : u[0]);
+// The group's seven thresholds, u_k <-> midpoint k in (0.25 >, 0.75 >=, 1.25 >, 1.75 >=,
+// 2.5 >, 3.5 >=, 5 >).
+struct Thresholds {
+    uint32_t u0, u1, u2, u3, u4, u5, u6;
+};
+
+// Magnitude code of a bf16 magnitude a16: a three-level binary search over the thresholds.
+// The thresholds come by value: selecting between members of a referenced struct is
+// turned into a computed-offset load, which keeps the struct in private memory.
+__device__ inline uint32_t e2m1_mag(uint32_t a16, const Thresholds t) {
+    const uint32_t c1 = a16 > t.u3;
+    const uint32_t c2 = a16 > (c1 ? t.u5 : t.u1);
+    const uint32_t t3 = c1 ? (c2 ? t.u6 : t.u4) : (c2 ? t.u2 : t.u0);
     const uint32_t c3 = a16 > t3;
     return (c1 << 2) | (c2 << 1) | c3;
 }
@@ -108,14 +115,13 @@ __device__ inline uint32_t quantize_group(const uint32_t (&w)[8], double g, uint
     if (g > 0.0 && amax > 0.0) sc = e4m3_code_exact(amax, 6.0 * g);
     const double Sg = e4m3_pos_value(sc) * g;        // exact (<= 28 significant bits)
 
-    uint32_t u[7];
+    Thresholds u;
     if (Sg > 0.0) {
-        u[0] = thr_gt(0.25 * Sg); u[1] = thr_ge(0.75 * Sg); u[2] = thr_gt(1.25 * Sg);
-        u[3] = thr_ge(1.75 * Sg); u[4] = thr_gt(2.5 * Sg);  u[5] = thr_ge(3.5 * Sg);
-        u[6] = thr_gt(5.0 * Sg);
+        u.u0 = thr_gt(0.25 * Sg); u.u1 = thr_ge(0.75 * Sg); u.u2 = thr_gt(1.25 * Sg);
+        u.u3 = thr_ge(1.75 * Sg); u.u4 = thr_gt(2.5 * Sg);  u.u5 = thr_ge(3.5 * Sg);
+        u.u6 = thr_gt(5.0 * Sg);
     } else {
-#pragma unroll
-        for (int k = 0; k < 7; ++k) u[k] = 0xFFFFu;  // every magnitude 0
+        u.u0 = u.u1 = u.u2 = u.u3 = u.u4 = u.u5 = u.u6 = 0xFFFFu;   // every magnitude 0
     }
     packed[0] = packed[1] = 0u;
 #pragma unroll
