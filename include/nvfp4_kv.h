@@ -99,8 +99,9 @@ int nvfp4_kv_calibrate(const nvfp4_kv_cache *cache, const void *k_rows, const vo
  *   k_new, v_new:  device bf16 [sum(n_new)][num_kv_heads][head_dim], concatenated over b
  *   global_scale:  device float [num_seqs][num_kv_heads][2]
  *   seq_base, write_pos, n_new: host int64 [num_seqs]; n_new[b] >= 0
- * Errors: EINVAL, EUNSUPPORTED (num_seqs > 8, head_dim), ERANGE (a slot outside
- *         [0, capacity)). Sequences must not write overlapping slots. */
+ * Errors: EINVAL, EUNSUPPORTED (num_seqs > 8, head_dim, sum(n_new) * head_dim / 8
+ *         above 2^31 - 1), ERANGE (a slot outside [0, capacity)). Sequences must not
+ *         write overlapping slots. */
 int nvfp4_kv_append(const nvfp4_kv_cache *cache, const void *k_new, const void *v_new,
                     const float *global_scale, int32_t num_seqs, const int64_t *seq_base,
                     const int64_t *write_pos, const int64_t *n_new, void *stream);

@@ -243,6 +243,9 @@ int nvfp4_kv_append(const nvfp4_kv_cache *cache, const void *k_new, const void *
     }
     for (int b = num_seqs; b <= nvfp4::kMaxSeqs; ++b) p.row_start[b] = acc;
     if (acc == 0) return ok();
+    if (acc * (cache->head_dim / 8) > INT32_MAX)
+        return fail(NVFP4_EUNSUPPORTED, "%lld rows in one append call (at most %d for head_dim %d)", (long long)acc,
+                    INT32_MAX / (cache->head_dim / 8), cache->head_dim);
     if (!aligned16(k_new) || !aligned16(v_new)) return fail(NVFP4_EINVAL, "k_new/v_new must be non-null and 16-byte aligned");
     p.k_new = static_cast<const uint16_t *>(k_new);
     p.v_new = static_cast<const uint16_t *>(v_new);

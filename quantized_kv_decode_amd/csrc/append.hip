@@ -12,32 +12,33 @@ namespace {
 
 using namespace dev;
 
-// One thread per (row, head, K|V, group of 16).
+// One thread per (row, K|V, group of 16) of KV head blockIdx.y. Every divisor of the
+// index decomposition is a compile-time constant (head_dim is a template parameter;
+// divisions by run-time values cost tens of instructions each).
+template <int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-    const int groups = p.D / 16;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t per_kv = p.rows * p.Hkv * groups;
-    if (tid >= 2 * per_kv) return;
-    const int kv = tid >= per_kv;                     // 0 = K, 1 = V
-    const int64_t t = tid - kv * per_kv;
-    const int j = (int)(t % groups);
-    const int h = (int)((t / groups) % p.Hkv);
-    const int64_t r = t / ((int64_t)groups * p.Hkv);
+    constexpr int groups = D / 16;
+    const uint32_t tx = blockIdx.x * 256u + threadIdx.x;
+    if (tx >= (uint32_t)(p.rows * 2 * groups)) return;
+    const int h = blockIdx.y;
+    const int j = tx % groups;
+    const int kv = (tx / groups) & 1;                 // 0 = K, 1 = V
+    const int64_t r = tx / (2 * groups);
     int b = 0;
 #pragma unroll
     for (int s = 1; s < kMaxSeqs; ++s)
         if (s < p.B && r >= p.row_start[s]) b = s;
     const int64_t slot = p.dst_start[b] + (r - p.row_start[b]);
 
-    const uint16_t *src = (kv ? p.v_new : p.k_new) + (r * p.Hkv + h) * p.D + 16 * j;
+    const uint16_t *src = (kv ? p.v_new : p.k_new) + (r * p.Hkv + h) * D + 16 * j;
     const uint4 w0 = *reinterpret_cast<const uint4 *>(src);
     const uint4 w1 = *reinterpret_cast<const uint4 *>(src + 8);
     const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 
     uint32_t packed[2];
-    const uint32_t sc = quantize_group(w, (double)p.gscale[(b * p.Hkv + h) * 2 + kv], packed);
+    const uint32_t sc = quantize_group(w, p.gscale[(b * p.Hkv + h) * 2 + kv], packed);
     const int64_t plane_row = (int64_t)h * p.cap + slot;
-    uint8_t *codes = (kv ? p.vc : p.kc) + plane_row * (p.D / 2) + 8 * j;
+    uint8_t *codes = (kv ? p.vc : p.kc) + plane_row * (D / 2) + 8 * j;
     *reinterpret_cast<uint2 *>(codes) = make_uint2(packed[0], packed[1]);
     (kv ? p.vs : p.ks)[plane_row * groups + j] = (uint8_t)sc;
 }
@@ -89,10 +90,15 @@ __global__ __launch_bounds__(64) void calib_finalize_kernel(float *g, int n) {
 }  // namespace
 
 hipError_t launch_append(const AppendParams &p, hipStream_t s) {
-    const int64_t threads = 2 * p.rows * p.Hkv * (p.D / 16);
-    if (threads == 0) return hipSuccess;
-    const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    if (p.rows == 0) return hipSuccess;
+    const int64_t threads = p.rows * 2 * (p.D / 16);  // per KV head; < 2^31 (checked by the caller)
+    const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)p.Hkv);
+    if (p.D == 256)
+        hipLaunchKernelGGL(append_kernel<256>, grid, dim3(256), 0, s, p);
+    else if (p.D == 128)
+        hipLaunchKernelGGL(append_kernel<128>, grid, dim3(256), 0, s, p);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -110,7 +110,7 @@ __device__ inline void append_step_rows(const DecodeParams &p, int b, int kh, in
         const uint4 w1 = *reinterpret_cast<const uint4 *>(src + 8);
         const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         uint32_t packed[2];
-        const uint32_t sc = quantize_group(w, (double)p.gscale[(b * p.Hkv + kh) * 2 + kv], packed);
+        const uint32_t sc = quantize_group(w, p.gscale[(b * p.Hkv + kh) * 2 + kv], packed);
         const int64_t plane_row = (int64_t)kh * p.cap + p.seq_base[b] + L - p.n_q + r;
         *reinterpret_cast<uint2 *>((kv ? p.vc : p.kc) + plane_row * (D / 2) + 8 * j) = make_uint2(packed[0], packed[1]);
         (kv ? p.vs : p.ks)[plane_row * groups + j] = (uint8_t)sc;

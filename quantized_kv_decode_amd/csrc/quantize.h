@@ -8,17 +8,22 @@
 // Rounding is decided on exact reals. The group scale is the E4M3 value nearest
 // amax/(6g) (ties to the even code, saturating at 448); each element's magnitude
 // is the E2M1 value nearest |x|/(S g) (ties to the even code, saturating at 6).
-// How the decisions are made exact:
-//   * scale: a candidate from the fp64 quotient, then one correction against the
-//     neighbouring midpoints m with exact fp64 products m * 6g (<= 31 bits);
+// Everything is branch-free (one thread handles one group, so the cost is the
+// instruction count). How the decisions are made exact:
+//   * scale: an approximate quotient gives the code c whose value is the largest
+//     not above it; the exact code is c or c + 1 (the quotient is accurate to far
+//     better than the 1/32 relative half-gap of E4M3), settled by one test against
+//     the midpoint m(c, c+1), whose product with 6g is exact in fp64 (<= 32 bits);
 //   * elements: the seven E2M1 midpoints t (0.25 ... 5) give thresholds T = t S g,
 //     exact in fp64 (<= 31 bits). A bf16 input a compared with T is an fp32 value,
 //     so "a > T" equals "a > rd32(T)" and "a >= T" equals "a > pred32(ru32(T))",
 //     with rd32/ru32 the directed roundings to fp32. For non-negative floats the
 //     order is the unsigned order of the bit patterns, and an fp32 threshold U
 //     compares with a bf16 magnitude a16 as (a16 << 16) > U  <=>  a16 > (U >> 16).
-//     So each group yields seven 16-bit integer thresholds and every element is
+//     So each group yields seven 16-bit integer thresholds, and every element is
 //     classified by integer compares alone (exact, independent of denormal modes).
+//     The compares run on two elements at once in 16-bit lanes: with u <= 0x7F80
+//     and a16 <= 0x7FFF, the lane u - a16 is negative (bit 15 set) iff a16 > u.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,109 +33,103 @@
 namespace nvfp4 {
 namespace dev {
 
-// E4M3FN value of a non-negative code 0x00..0x7E: exponent field 0 is subnormal.
-__device__ inline double e4m3_pos_value(int c) {
-    const int e = c >> 3, m = c & 7;
-    return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
-}
-
-// Nearest E4M3 code to amax / b6 (b6 = 6 g > 0, exact), ties to even, saturating.
-__device__ inline int e4m3_code_exact(double amax, double b6) {
-    const double q = amax / b6;                       // correctly rounded fp64
-    int c;
-    if (!(q < 448.0)) {
-        c = 0x7E;
-    } else if (q < 0.015625) {                        // below 2^-6: subnormal spacing 2^-9
-        c = (int)rint(q * 512.0);                     // 0..8 (8 = 2^-6, the first normal)
-    } else {
-        int e;
-        const double f = frexp(q, &e);                // q = f * 2^e, f in [0.5, 1)
-        const int m = (int)rint(f * 16.0) - 8;        // 3-bit mantissa, may carry to 8
-        c = ((e + 6) << 3) + m;                       // exponent field e - 1 + 7
-        if (c > 0x7E) c = 0x7E;
-    }
-    // The fp64 quotient differs from the exact one by < 1 ulp, so the candidate is
-    // at most one code away; settle with the exact midpoint tests.
-    if (c < 0x7E) {
-        const double up = 0.5 * (e4m3_pos_value(c) + e4m3_pos_value(c + 1)) * b6;
-        if (amax > up || (amax == up && ((c + 1) & 1) == 0)) return c + 1;
-    }
-    if (c > 0) {
-        const double dn = 0.5 * (e4m3_pos_value(c - 1) + e4m3_pos_value(c)) * b6;
-        if (amax < dn || (amax == dn && ((c - 1) & 1) == 0)) return c - 1;
-    }
-    return c;
-}
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-// Round a positive double to fp32 downward / upward.
-__device__ inline float rd32(double t) {
-    float f = (float)t;
-    if ((double)f > t) f = nextafterf(f, 0.0f);
-    return f;
-}
-__device__ inline float ru32(double t) {
-    float f = (float)t;
-    if ((double)f < t) f = nextafterf(f, INFINITY);
-    return f;
-}
+// E4M3FN code c (0..0x7E) has the value sig * 2^(ex - 10): exponent field 0 is
+// subnormal (sig = mantissa, ex = 1), otherwise sig = 8 + mantissa, ex = field.
+__device__ inline int e4m3_sig(int c) { return (c & 7) | (c >= 8 ? 8 : 0); }
+__device__ inline int e4m3_ex(int c) { return c >= 8 ? (c >> 3) : 1; }
 
-// 16-bit threshold for "a > t*Sg" (strict: ties go down) and "a >= t*Sg" (ties go up).
-__device__ inline uint32_t thr_gt(double T) { return f32_bits(rd32(T)) >> 16; }
-__device__ inline uint32_t thr_ge(double T) {
-    const float u = ru32(T);
-    return f32_bits(nextafterf(u, 0.0f)) >> 16;     // u > 0 here
+// Nearest E4M3 code to amax / (6 g), ties to even, saturating; amax > 0, g > 0.
+__device__ inline int e4m3_code_exact(double amax, double gd) {
+    const double q = fmin(amax * __builtin_amdgcn_rcp(6.0 * gd), 448.0);
+    const float q32 = (float)q;
+    // Largest code whose value is at most q32 (values are monotone in the bits).
+    const int c = q32 < 0.015625f ? (int)(q32 * 512.0f) : (int)(f32_bits(q32) >> 20) - 960;
+    // m(c, c+1) * 6g = (2 sig + 1) 2^(ex - 11) * 6g, exact.
+    const double mid = ldexp((double)(12 * e4m3_sig(c) + 6) * gd, e4m3_ex(c) - 11);
+    const int up = amax > mid || (amax == mid && (c & 1));   // tie: to the even one of c, c+1
+    return min(c + up, 0x7E);
 }
 
-// The group's seven thresholds, u_k <-> midpoint k in (0.25 >, 0.75 >=, 1.25 >, 1.75 >=,
-// 2.5 >, 3.5 >=, 5 >).
-struct Thresholds {
-    uint32_t u0, u1, u2, u3, u4, u5, u6;
-};
+// Both 16-bit lanes = the threshold for "a > T" (strict) or "a >= T".
+__device__ inline uint32_t thr_pair(double T, bool strict) {
+    const float f = (float)T;                         // to nearest
+    const double back = (double)f;
+    // strict: rd32(T) = f, or its predecessor when f rounded up;
+    // else:   pred32(ru32(T)) = f's predecessor, or f when f rounded down.
+    const uint32_t bits = f32_bits(f) - (uint32_t)(strict ? back > T : back >= T);
+    return __builtin_amdgcn_perm(bits, bits, 0x03020302u);   // high half, twice
+}
 
-// Magnitude code of a bf16 magnitude a16: a three-level binary search over the thresholds.
-// The thresholds come by value: selecting between members of a referenced struct is
-// turned into a computed-offset load, which keeps the struct in private memory.
-__device__ inline uint32_t e2m1_mag(uint32_t a16, const Thresholds t) {
-    const uint32_t c1 = a16 > t.u3;
-    const uint32_t c2 = a16 > (c1 ? t.u5 : t.u1);
-    const uint32_t t3 = c1 ? (c2 ? t.u6 : t.u4) : (c2 ? t.u2 : t.u0);
-    const uint32_t c3 = a16 > t3;
-    return (c1 << 2) | (c2 << 1) | c3;
+__device__ inline uint32_t pk_sub16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, a) - __builtin_bit_cast(u16x2_t, b));
+}
+// 0xFFFF in each lane whose bit 15 is set. The empty asm hides that the result is a
+// lane mask: knowing it, the compiler turns each bit select on it into two 16-bit
+// selects and a repack (five instructions instead of one).
+__device__ inline uint32_t pk_sign16(uint32_t a) {
+    uint32_t m = __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2_t, a) >> (short)15);
+    asm("" : "+v"(m));
+    return m;
+}
+__device__ inline uint32_t pk_max16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                  __builtin_bit_cast(u16x2_t, b)));
+}
+__device__ inline uint32_t sel(uint32_t m, uint32_t x, uint32_t y) { return (m & x) | (~m & y); }
+
+// Codes of the two elements of P (bf16 e in the low lane, e + 4 in the high lane),
+// placed at nibble e of each 16-bit half: a three-level binary search over u[0..6].
+template <int E>
+__device__ inline uint32_t e2m1_pair(uint32_t P, const uint32_t (&u)[7]) {
+    const uint32_t A = P & 0x7FFF7FFFu;
+    const uint32_t m1 = pk_sign16(pk_sub16(u[3], A));
+    const uint32_t m2 = pk_sign16(pk_sub16(sel(m1, u[5], u[1]), A));
+    const uint32_t s3 = pk_sub16(sel(m1, sel(m2, u[6], u[4]), sel(m2, u[2], u[0])), A);
+    constexpr uint32_t one = 0x00010001u << (4 * E);
+    return (m1 & (one << 2)) | (m2 & (one << 1)) | ((s3 >> (15 - 4 * E)) & one) |
+           ((P >> (12 - 4 * E)) & (one << 3));
 }
 
 // One group: w holds 16 bf16 values (element 2k in the low half of word k), g the
 // global scale. Returns the E4M3 scale code; packed receives the 16 E2M1 codes,
 // element 2j in the low nibble of byte j.
-__device__ inline uint32_t quantize_group(const uint32_t (&w)[8], double g, uint32_t (&packed)[2]) {
-    uint32_t amax16 = 0;
+__device__ inline uint32_t quantize_group(const uint32_t (&w)[8], float g, uint32_t (&packed)[2]) {
+    // Pair element n (of each half of the group) with element n + 4, so that both
+    // lanes of a pair land on the same nibble of their half of the packed word.
+    uint32_t P[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        amax16 = max(amax16, w[k] & 0x7FFFu);
-        amax16 = max(amax16, (w[k] >> 16) & 0x7FFFu);
+    for (int h = 0; h < 2; ++h) {
+        P[4 * h + 0] = __builtin_amdgcn_perm(w[4 * h + 2], w[4 * h + 0], 0x05040100u);
+        P[4 * h + 1] = __builtin_amdgcn_perm(w[4 * h + 2], w[4 * h + 0], 0x07060302u);
+        P[4 * h + 2] = __builtin_amdgcn_perm(w[4 * h + 3], w[4 * h + 1], 0x05040100u);
+        P[4 * h + 3] = __builtin_amdgcn_perm(w[4 * h + 3], w[4 * h + 1], 0x07060302u);
     }
-    const double amax = (double)__builtin_bit_cast(float, amax16 << 16);
-    int sc = 0;
-    if (g > 0.0 && amax > 0.0) sc = e4m3_code_exact(amax, 6.0 * g);
-    const double Sg = e4m3_pos_value(sc) * g;        // exact (<= 28 significant bits)
+    uint32_t mx = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mx = pk_max16(mx, P[k] & 0x7FFF7FFFu);
+    const uint32_t amax16 = max(mx & 0xFFFFu, mx >> 16);
 
-    Thresholds u;
-    if (Sg > 0.0) {
-        u.u0 = thr_gt(0.25 * Sg); u.u1 = thr_ge(0.75 * Sg); u.u2 = thr_gt(1.25 * Sg);
-        u.u3 = thr_ge(1.75 * Sg); u.u4 = thr_gt(2.5 * Sg);  u.u5 = thr_ge(3.5 * Sg);
-        u.u6 = thr_gt(5.0 * Sg);
-    } else {
-        u.u0 = u.u1 = u.u2 = u.u3 = u.u4 = u.u5 = u.u6 = 0xFFFFu;   // every magnitude 0
-    }
-    packed[0] = packed[1] = 0u;
+    const double gd = (double)g;
+    const double amax = (double)__builtin_bit_cast(float, amax16 << 16);
+    const int sc = (g > 0.0f && amax16 != 0) ? e4m3_code_exact(amax, gd) : 0;
+    // S g, exact (<= 28 significant bits); a zero scale maps every magnitude to 0,
+    // which the infinite thresholds give.
+    const double Sg = sc ? ldexp((double)e4m3_sig(sc) * gd, e4m3_ex(sc) - 10) : (double)INFINITY;
+
+    uint32_t u[7];
+    u[0] = thr_pair(0.25 * Sg, true);  u[1] = thr_pair(0.75 * Sg, false);
+    u[2] = thr_pair(1.25 * Sg, true);  u[3] = thr_pair(1.75 * Sg, false);
+    u[4] = thr_pair(2.5 * Sg, true);   u[5] = thr_pair(3.5 * Sg, false);
+    u[6] = thr_pair(5.0 * Sg, true);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t lo = w[k] & 0xFFFFu, hi = w[k] >> 16;
-        const uint32_t c0 = e2m1_mag(lo & 0x7FFFu, u) | ((lo >> 12) & 8u);
-        const uint32_t c1 = e2m1_mag(hi & 0x7FFFu, u) | ((hi >> 12) & 8u);
-        packed[k >> 2] |= (c0 | (c1 << 4)) << (8 * (k & 3));
-    }
+    for (int h = 0; h < 2; ++h)
+        packed[h] = e2m1_pair<0>(P[4 * h + 0], u) | e2m1_pair<1>(P[4 * h + 1], u) |
+                    e2m1_pair<2>(P[4 * h + 2], u) | e2m1_pair<3>(P[4 * h + 3], u);
     return (uint32_t)sc;
 }
 
