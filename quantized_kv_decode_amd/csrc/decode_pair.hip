@@ -141,7 +141,7 @@ void decode_pair_kernel(DecodeParams p) {
     constexpr int EPL = D / 16;
     using LD = PairLds<D, NT>;
     __shared__ __attribute__((aligned(16))) uint8_t big[LD::BIG];
-    __shared__ __attribute__((aligned(16))) u32x4_t pbuf[kPairs][NT][64];   // (mt 0 | mt 1) fp16 P per lane
+    __shared__ __attribute__((aligned(16))) u32x4_t pbuf[kPairs][2][NT][64];   // [pair][parity]: fp16 P per lane
     __shared__ float xmax[kPairs][2][2][NT * 16];                         // [pair][parity][half]
     __shared__ float sm_c[kMaxRows];
     __shared__ float sm_m[kPairs][kMaxRows];
@@ -257,55 +257,11 @@ void decode_pair_kernel(DecodeParams p) {
         }
     };
 
-    start_block(0);
-    for (int j = 0; j < iters; ++j) {
-        __syncthreads();                                   // A: row maxima of block j
-        bool need_any = false;
-        float mb[NT];
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            mb[rt] = fmaxf(mloc[rt], xmax[pair][j & 1][1 - w][16 * rt + n]);
-            need_any |= mb[rt] > m[rt] + kLazyMax;
-        }
-        // both waves of the pair see the same maxima and m, so they decide alike
-        if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
-#pragma unroll
-            for (int rt = 0; rt < NT; ++rt) {
-                const bool need = mb[rt] > m[rt] + kLazyMax;
-                const float mnew = need ? mb[rt] : m[rt];
-                const float alpha = need ? exp2f(m[rt] - mnew) : 1.0f;   // m = -inf -> 0
-                m[rt] = mnew;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * g + i);       // accumulator row 4 g + i
-                    lsum[rt][i] *= ai;
-#pragma unroll
-                    for (int t = 0; t < HT; ++t) acc[rt][t][i] *= ai;
-                }
-            }
-        }
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            const float mu = m[rt] == -INFINITY ? 0.0f : m[rt];
-            const half2_t p01 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][0] - mu),
-                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][1] - mu)};
-            const half2_t p23 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][2] - mu),
-                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][3] - mu)};
-            uint32_t *dst = reinterpret_cast<uint32_t *>(&pbuf[pair][rt][lane]) + 2 * w;
-            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{as_u32(p01), as_u32(p23)};
-        }
-        PairVPrep vp;
-        pair_v_prep<D>(vp, r);
-        __builtin_amdgcn_sched_barrier(0);
-        pair_load_v<D>(r, vc, vs, offs_for(pair + kPairs * (j + 1)));
-        if (j + 1 < iters) start_block(j + 1);
-        __syncthreads();                                   // B: probabilities of block j
+    // O += P(j) . V(j) over this wave's half of head_dim, P(j) of both waves from LDS.
+    auto pv_block = [&](int j, const PairVPrep &vp) __attribute__((always_inline)) {
         half8_t pa[NT];
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) pa[rt] = __builtin_bit_cast(half8_t, pbuf[pair][rt][lane]);
-
-        // ---- O += P(j) . V(j) over this wave's half of head_dim
+        for (int rt = 0; rt < NT; ++rt) pa[rt] = __builtin_bit_cast(half8_t, pbuf[pair][j & 1][rt][lane]);
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
             uint32_t bw[4];
@@ -331,7 +287,65 @@ void decode_pair_kernel(DecodeParams p) {
             for (int rt = 0; rt < NT; ++rt)
                 lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], ones, lsum[rt], 0, 0, 0);
         }
-    }
+    };
+
+    // One loop trip per block j of the pair, with ONE workgroup barrier: it publishes the
+    // row maxima of block j and the probabilities of block j - 1 of both waves. After it,
+    // each wave fixes the reference m for block j, writes P(j) (LDS, parity j & 1), multiplies
+    // P(j - 1) into O, interleaves V(j), issues the loads of block j + 1 and computes S^T of
+    // block j + 1 -- one straight stretch of independent matrix and vector work. The rare
+    // rescale of O by exp2(m_old - m_new) comes last: O then holds blocks up to j - 1, all
+    // relative to m_old, and P(j) (relative to m_new) is multiplied in on the next trip.
+    PairVPrep vprev;
+    auto trip = [&](int j, bool do_pv, bool do_next) __attribute__((always_inline)) {
+        __syncthreads();
+        bool need_any = false;
+        float alpha[NT];
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const float mb = fmaxf(mloc[rt], xmax[pair][j & 1][1 - w][16 * rt + n]);
+            const bool need = mb > m[rt] + kLazyMax;   // both waves of the pair see the same values
+            const float mnew = need ? mb : m[rt];
+            alpha[rt] = need ? exp2f(m[rt] - mnew) : 1.0f;   // m = -inf -> 0
+            m[rt] = mnew;
+            need_any |= need;
+        }
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const float mu = m[rt] == -INFINITY ? 0.0f : m[rt];
+            const half2_t p01 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][0] - mu),
+                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][1] - mu)};
+            const half2_t p23 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][2] - mu),
+                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][3] - mu)};
+            uint32_t *dst = reinterpret_cast<uint32_t *>(&pbuf[pair][j & 1][rt][lane]) + 2 * w;
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{as_u32(p01), as_u32(p23)};
+        }
+        if (do_pv) pv_block(j - 1, vprev);
+        pair_v_prep<D>(vprev, r);
+        __builtin_amdgcn_sched_barrier(0);
+        pair_load_v<D>(r, vc, vs, offs_for(pair + kPairs * (j + 1)));
+        if (do_next) start_block(j + 1);
+        if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha[rt], 4 * g + i);   // accumulator row 4 g + i
+                    lsum[rt][i] *= ai;
+#pragma unroll
+                    for (int t = 0; t < HT; ++t) acc[rt][t][i] *= ai;
+                }
+            }
+        }
+    };
+
+    start_block(0);
+    trip(0, false, iters > 1);
+    for (int j = 1; j < iters - 1; ++j) trip(j, true, true);
+    if (iters > 1) trip(iters - 1, true, false);
+    __syncthreads();                                       // P of the last block
+    pv_block(iters - 1, vprev);
 
     // ---- merge the two pairs and write the unit's partial
 #pragma unroll
