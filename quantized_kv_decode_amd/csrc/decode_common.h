@@ -62,6 +62,17 @@ struct Offs {
     uint32_t kc, ks, vc, vs;
 };
 
+// Byte offsets of a block starting at token slot slot0: lane part + slot part (32-bit:
+// a head plane is below 2^31 bytes).
+__device__ inline Offs add_slot(const Offs &lane, uint32_t slot0, int D) {
+    Offs o;
+    o.kc = lane.kc + slot0 * (uint32_t)(D / 2);
+    o.ks = lane.ks + slot0 * (uint32_t)(D / 16);
+    o.vc = lane.vc + slot0 * (uint32_t)(D / 2);
+    o.vs = lane.vs + slot0 * (uint32_t)(D / 16);
+    return o;
+}
+
 // Head planes are below 2^31 bytes (the capacity limit), so this offset, plus any
 // immediate offset of a block's loads, is out of range for every plane.
 constexpr uint32_t kPastPlane = 0x80000000u;

@@ -85,15 +85,6 @@ __device__ inline Offs pair_lane_offsets(int w, int g, int n) {
     return o;
 }
 
-__device__ inline Offs add_slot(const Offs &lane, uint32_t slot0, int D) {
-    Offs o;
-    o.kc = lane.kc + slot0 * (uint32_t)(D / 2);
-    o.ks = lane.ks + slot0 * (uint32_t)(D / 16);
-    o.vc = lane.vc + slot0 * (uint32_t)(D / 2);
-    o.vs = lane.vs + slot0 * (uint32_t)(D / 16);
-    return o;
-}
-
 template <int D>
 __device__ inline half8_t pair_dequant_k(const PairRaw<D> &r, int kk) {
     const uint32_t w = r.k[kk];
