@@ -4,6 +4,8 @@ The oracle side and the GPU side only share the seeded inputs from `workloads`.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -90,3 +92,51 @@ def assert_planes_equal(pool, cache: oracle.Cache):
 
 def max_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.abs(got.astype(np.float64) - ref).max())
+
+
+def _bf16_u16(x):
+    return workloads.as_u16(torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16))
+
+
+def _bf16_neighbours(vals):
+    """Every bf16 value in vals plus the bf16 values one ulp either side."""
+    u = _bf16_u16(vals).astype(np.int32)
+    out = np.concatenate([u, u + 1, np.maximum(u - 1, 0)]) & 0x7FFF
+    sign = np.arange(out.size) % 2 == 1
+    return (out | (sign.astype(np.int32) << 15)).astype(np.uint16)
+
+
+def adversarial_rows(D=256):
+    """Groups whose maxima sit on every E4M3 midpoint (times 6) and whose elements sit
+    on every E2M1 midpoint of their scale, with bf16 neighbours, signed zeros, zero
+    groups and saturating values, for g = 1 (so every tie is representable)."""
+    e4 = [oracle.e4m3_value(c) for c in range(127)]
+    groups = []
+    for k in range(126):                                     # scale ties and their neighbours
+        mid = 0.5 * (e4[k] + e4[k + 1])
+        amax = _bf16_neighbours([6 * mid])
+        for a in amax:
+            grp = np.zeros(16, np.uint16)
+            grp[0] = a
+            grp[1] = _bf16_u16([-mid])[0]
+            groups.append(grp)
+    thr = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 3.0, 6.0]
+    for c in (1, 2, 7, 8, 0x30, 0x38, 0x3A, 0x55, 0x70, 0x7E):   # element ties under several scales
+        S = e4[c]
+        vals = _bf16_neighbours([t * S for t in thr])
+        for i in range(0, vals.size, 15):
+            grp = np.zeros(16, np.uint16)
+            grp[0] = _bf16_u16([6 * S])[0]
+            chunk = vals[i:i + 15]
+            grp[1:1 + chunk.size] = chunk
+            groups.append(grp)
+    groups.append(np.zeros(16, np.uint16))                     # +0 group
+    groups.append(np.full(16, 0x8000, np.uint16))              # -0 group
+    groups.append(_bf16_u16([3e4, -3e4, 1e5, 7, -1e-3] + [0] * 11))    # saturating
+    groups.append(_bf16_u16([1e-38, -3e-39, 1e-40] + [0] * 13))        # bf16 subnormals
+    n = len(groups)
+    per_row = D // 16
+    rows = int(math.ceil(n / per_row))
+    flat = np.zeros((rows * per_row, 16), np.uint16)
+    flat[:n] = np.stack(groups)
+    return flat.reshape(rows, D)
