@@ -152,6 +152,31 @@ int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, co
                       int32_t n_q, int32_t num_q_heads, float sm_scale, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/* The decode step with the lengths in device memory (knoopx/ninfer page, "Capabilities and
+ * limits": decode replayed as exact-batch graphs). The kernels read seq_len_dev when they
+ * run, so a HIP graph that captured this call replays across decode steps while the
+ * sequences grow: the caller updates seq_len_dev (and the contents of q, k_new, v_new)
+ * between replays. The launch configuration is fixed by max_len: the split planner runs on
+ * max_len on the host; each kernel divides a sequence's fixed number of units over the
+ * length it reads (units past it are empty). Per replay, the result equals
+ * nvfp4_decode_step with seq_len = the device values (same pool bytes; out within the
+ * attention tolerance, the split points may differ).
+ *   max_len:     host int64 [num_seqs], an upper bound on every seq_len_dev[b] the graph
+ *                will see; validated as seq_len is for nvfp4_decode_step (n_q <= max_len,
+ *                seq_base + max_len within capacity); it sizes the workspace:
+ *                nvfp4_decode_attn_workspace_bytes(cache, num_seqs, max_len, n_q, num_q_heads)
+ *   seq_len_dev: device int64 [num_seqs], 8-byte aligned; read at run time. A value outside
+ *                [n_q, max_len[b]] is a caller error: the kernels clamp it into that range
+ *                (no access outside the sequence's slots; the result is then meaningless).
+ *   k_new, v_new: as for nvfp4_decode_step, or both null: attention only, no append.
+ *   Other arguments, the workspace and the errors as for nvfp4_decode_step (EINVAL also
+ *   for a null or unaligned seq_len_dev, or only one of k_new / v_new null). */
+int nvfp4_decode_step_dev_len(const nvfp4_kv_cache *cache, const float *global_scale, const void *k_new,
+                              const void *v_new, const void *q, void *out, int32_t out_dtype,
+                              int32_t num_seqs, const int64_t *seq_base, const int64_t *max_len,
+                              const int64_t *seq_len_dev, int32_t n_q, int32_t num_q_heads,
+                              float sm_scale, void *workspace, size_t workspace_bytes, void *stream);
+
 /* The two kernels of nvfp4_decode_attn, callable on their own (same arguments,
  * same workspace) so that each can be timed: the split-K partial pass writes
  * per-split (o, m, l) into the workspace; the combine pass merges them by

@@ -65,12 +65,14 @@ def load_library():
     lib.nvfp4_decode_attn_workspace_bytes.restype = sz
     lib.nvfp4_decode_attn.argtypes = [P, vp, vp, vp, i32, i32, i64, i64, i32, i32, f32, vp, sz, vp]
     lib.nvfp4_decode_step.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, i64, i64, i32, i32, f32, vp, sz, vp]
+    lib.nvfp4_decode_step_dev_len.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, i64, i64, vp, i32, i32, f32, vp, sz,
+                                              vp]
     lib.nvfp4_decode_attn_partial.argtypes = [P, vp, vp, i32, i64, i64, i32, i32, f32, vp, sz, vp]
     lib.nvfp4_decode_attn_combine.argtypes = [P, vp, vp, i32, i32, i64, i32, i32, vp, sz, vp]
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_last_error.restype = ctypes.c_char_p
     for f in ("nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn", "nvfp4_decode_step",
-              "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine"):
+              "nvfp4_decode_step_dev_len", "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -189,6 +191,26 @@ def decode_step(pool: KVPool, global_scale: torch.Tensor, k_new: torch.Tensor, v
     _check(load_library().nvfp4_decode_step(ctypes.byref(d), _ptr(global_scale), _ptr(k_new), _ptr(v_new), _ptr(q),
                                             _ptr(out), code, B, _i64(seq_base), _i64(seq_len), n_q, Hq,
                                             float(sm_scale), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_step_dev_len(pool: KVPool, global_scale: torch.Tensor, k_new, v_new, q: torch.Tensor, seq_base, max_len,
+                        seq_len_dev: torch.Tensor, sm_scale: float, out: torch.Tensor | None = None,
+                        out_dtype=torch.float32, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """decode_step with the lengths in device memory (int64 tensor [B] on the GPU, read when the kernels
+    run), so that a captured graph replays across steps; max_len (host) bounds every length and fixes the
+    launch. k_new / v_new may both be None (attention only)."""
+    B, n_q, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, n_q, Hq, D), dtype=out_dtype, device=q.device)
+    code = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    if workspace is None:
+        workspace = alloc_workspace(pool, max_len, n_q, Hq, q.device)
+    d = pool.desc()
+    _check(load_library().nvfp4_decode_step_dev_len(
+        ctypes.byref(d), _ptr(global_scale), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), code, B, _i64(seq_base),
+        _i64(max_len), _ptr(seq_len_dev), n_q, Hq, float(sm_scale), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
     return out
 
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <string>
 
@@ -323,6 +324,43 @@ int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, co
     if (!std::isfinite(sm_scale)) return fail(NVFP4_EINVAL, "sm_scale must be finite");
     nvfp4::DecodeParams dp;
     fill_decode(dp, pl, cache, global_scale, q, seq_base, seq_len, sm_scale, workspace);
+    dp.k_new = static_cast<const uint16_t *>(k_new);
+    dp.v_new = static_cast<const uint16_t *>(v_new);
+    dp.out = out;
+    dp.out_bf16 = out_dtype == NVFP4_OUT_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = nvfp4::launch_decode_partial(dp, pl.D, pl.NT, s);
+    if (e != hipSuccess) return hip_status(e, "decode partial launch");
+    return hip_status(nvfp4::launch_decode_combine(dp, pl.D, s), "decode combine launch");
+}
+
+int nvfp4_decode_step_dev_len(const nvfp4_kv_cache *cache, const float *global_scale, const void *k_new,
+                              const void *v_new, const void *q, void *out, int32_t out_dtype, int32_t num_seqs,
+                              const int64_t *seq_base, const int64_t *max_len, const int64_t *seq_len_dev,
+                              int32_t n_q, int32_t num_q_heads, float sm_scale, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    // The plan (grid, units per sequence, workspace) comes from the upper bounds; the
+    // kernels split each sequence's units over the length they read from seq_len_dev.
+    nvfp4::SplitPlan pl;
+    if (!seq_base) return fail(NVFP4_EINVAL, "seq_base is null");
+    if (!max_len) return fail(NVFP4_EINVAL, "max_len is null");
+    int rc = make_plan(cache, num_seqs, seq_base, max_len, n_q, num_q_heads, pl);
+    if (rc) return rc;
+    if ((rc = check_decode_common(global_scale, workspace, workspace_bytes, pl))) return rc;
+    if (!seq_len_dev || reinterpret_cast<uintptr_t>(seq_len_dev) % 8 != 0)
+        return fail(NVFP4_EINVAL, "seq_len_dev must be non-null and 8-byte aligned");
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(NVFP4_EINVAL, "k_new and v_new must both be given or both be null");
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
+        return fail(NVFP4_EINVAL, "k_new and v_new must be 16-byte aligned");
+    if (!aligned16(q)) return fail(NVFP4_EINVAL, "q must be non-null and 16-byte aligned");
+    if (!aligned16(out)) return fail(NVFP4_EINVAL, "out must be non-null and 16-byte aligned");
+    if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16)
+        return fail(NVFP4_EINVAL, "out_dtype %d invalid", out_dtype);
+    if (!std::isfinite(sm_scale)) return fail(NVFP4_EINVAL, "sm_scale must be finite");
+    nvfp4::DecodeParams dp;
+    fill_decode(dp, pl, cache, global_scale, q, seq_base, max_len, sm_scale, workspace);
+    dp.len_dev = seq_len_dev;
     dp.k_new = static_cast<const uint16_t *>(k_new);
     dp.v_new = static_cast<const uint16_t *>(v_new);
     dp.out = out;

@@ -283,7 +283,7 @@ struct Lds {
     static constexpr int BYTES = Q_BYTES > MERGE_BYTES ? Q_BYTES : MERGE_BYTES;
 };
 
-template <int D, int NT>
+template <int D, int NT, bool DevLen>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_wgs_per_cu(NT))))
 void decode_partial_kernel(DecodeParams p) {
     constexpr int KK = D / 32;
@@ -295,7 +295,7 @@ void decode_partial_kernel(DecodeParams p) {
     __shared__ float sm_l[kWaves][kMaxRows];
 
     const int u = blockIdx.x;
-    const Unit un = unit_of(p, u);
+    const Unit un = unit_of<DevLen>(p, u);
     const int b = un.b, kh = un.kh, nblk = un.nblk;
     const int64_t L = un.L, t0 = un.t0;
 
@@ -557,7 +557,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 
 template <int D, int NT>
 hipError_t launch_partial_t(const DecodeParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_partial_kernel<D, NT>), dim3(p.units), dim3(256), 0, s, p);
+    if (p.len_dev != nullptr)
+        hipLaunchKernelGGL((decode_partial_kernel<D, NT, true>), dim3(p.units), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<D, NT, false>), dim3(p.units), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

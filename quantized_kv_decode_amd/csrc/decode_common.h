@@ -85,6 +85,9 @@ struct Unit {
     int64_t L, t0, t1;
 };
 
+// DevLen: the lengths are read from p.len_dev when the kernel runs (a separate kernel
+// instantiation, so that the host-length kernels carry none of its code).
+template <bool DevLen>
 __device__ inline Unit unit_of(const DecodeParams &p, int u) {
     Unit r;
     r.b = 0;
@@ -92,12 +95,32 @@ __device__ inline Unit unit_of(const DecodeParams &p, int u) {
     for (int s = 1; s < kMaxSeqs; ++s)
         if (s < p.B && u >= p.unit_base[s]) r.b = s;
     const int local = u - p.unit_base[r.b];
-    r.kh = local / p.n_split[r.b];
-    const int sp = local - r.kh * p.n_split[r.b];
-    r.L = p.seq_len[r.b];
-    r.last = sp == p.n_split[r.b] - 1;
-    r.t0 = (int64_t)sp * p.split_len[r.b];
-    r.t1 = r.last ? r.L : r.t0 + p.split_len[r.b];
+    const int ns = p.n_split[r.b];
+    r.kh = local / ns;
+    const int sp = local - r.kh * ns;
+    if constexpr (!DevLen) {
+        r.L = p.seq_len[r.b];
+        r.last = sp == ns - 1;
+        r.t0 = (int64_t)sp * p.split_len[r.b];
+        r.t1 = r.last ? r.L : r.t0 + p.split_len[r.b];
+    } else {
+        // Lengths read when the kernel runs (a captured graph replays across steps): the
+        // same split rule as the host planner, over the sequence's fixed number of units;
+        // units past the length are empty. Out-of-range lengths are clamped into
+        // [n_q, upper bound], so no access leaves the sequence's slots.
+        // readfirstlane: the loaded length is the same in every lane; without it the unit's
+        // range (and the block loop's control on both paths) would live in vector registers
+        const int Ld = __builtin_amdgcn_readfirstlane((int)min(max(p.len_dev[r.b], (int64_t)p.n_q), p.seq_len[r.b]));
+        const int L = Ld;
+        int sl = (L + ns - 1) / ns;
+        sl = (sl + kBlockTokens - 1) / kBlockTokens * kBlockTokens;
+        int ne = (L + sl - 1) / sl;
+        if (ne > 1 && L - (ne - 1) * sl < p.n_q) ne -= 1;    // the newest n_q tokens stay in one unit
+        r.L = L;
+        r.last = sp == ne - 1;
+        r.t0 = sp < ne ? (int64_t)sp * sl : (int64_t)L;
+        r.t1 = sp < ne ? (r.last ? (int64_t)L : r.t0 + sl) : (int64_t)L;
+    }
     r.nblk = (int)((r.t1 - r.t0 + kBlockTokens - 1) / kBlockTokens);
     return r;
 }

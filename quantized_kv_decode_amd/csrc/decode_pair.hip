@@ -124,7 +124,7 @@ struct PairLds {
     static constexpr int BIG = Q_BYTES > MERGE_BYTES ? Q_BYTES : MERGE_BYTES;
 };
 
-template <int D, int NT>
+template <int D, int NT, bool DevLen>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_wgs_per_cu(NT))))
 void decode_pair_kernel(DecodeParams p) {
     constexpr int KK = D / 32;
@@ -139,7 +139,7 @@ void decode_pair_kernel(DecodeParams p) {
     __shared__ float sm_l[kPairs][kMaxRows];
 
     const int u = blockIdx.x;
-    const Unit un = unit_of(p, u);
+    const Unit un = unit_of<DevLen>(p, u);
     const int b = un.b, kh = un.kh, nblk = un.nblk;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = wave >> 1, w = wave & 1;
@@ -210,7 +210,7 @@ void decode_pair_kernel(DecodeParams p) {
     //   barrier B  -> P(j) of both halves -> O += P(j) . V(j)
     // lim: offset limit of the block relative to L - n_q (32-bit: tokens < 2^31).
     const int lim0 = (int)(un.L - p.n_q - un.t0) - kBlockTokens * pair;
-    const int iters = (nblk + kPairs - 1) / kPairs;
+    const int iters = max((nblk + kPairs - 1) / kPairs, 1);   // an empty unit runs one masked trip
     float x[NT][4], mloc[NT];
 
     // S^T of the pair's block j from the K words in r, the K loads of block j + 1, and
@@ -401,7 +401,10 @@ void decode_pair_kernel(DecodeParams p) {
 
 template <int D, int NT>
 hipError_t launch_pair_t(const DecodeParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((decode_pair_kernel<D, NT>), dim3(p.units), dim3(256), 0, s, p);
+    if (p.len_dev != nullptr)
+        hipLaunchKernelGGL((decode_pair_kernel<D, NT, true>), dim3(p.units), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_pair_kernel<D, NT, false>), dim3(p.units), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

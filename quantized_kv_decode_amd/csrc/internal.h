@@ -38,6 +38,8 @@ struct DecodeParams {
     const float *gscale;                 // [B][Hkv][2]
     const uint16_t *q;                   // bf16 [B][n_q][Hq][D]
     const uint16_t *k_new, *v_new;       // bf16 [B n_q][Hkv][D] rows to append first, or null
+    const int64_t *len_dev;              // device lengths [B] read at run time, or null (then
+                                         // seq_len holds the lengths; else their upper bounds)
     float *ws_o, *ws_m, *ws_l;           // [units][R][D], [units][R], [units][R]
     void *out;
     int32_t out_bf16;

@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn_workspace_bytes", "nvfp4_decode_attn",
-              "nvfp4_decode_step", "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine", "nvfp4_last_error"):
+              "nvfp4_decode_step", "nvfp4_decode_step_dev_len", "nvfp4_decode_attn_partial",
+              "nvfp4_decode_attn_combine", "nvfp4_last_error"):
         assert f in names
 
 
@@ -143,6 +144,26 @@ def test_decode_step_validation_codes(lib):
     assert call(lens=(0,)) == qk.ERANGE
     assert call(base=(950,)) == qk.ERANGE
     assert call(ws=16) == qk.EWORKSPACE
+
+
+def test_decode_step_dev_len_validation_codes(lib):
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk)
+    a = 0x600000
+
+    def call(k=a, v=a, q=0x200000, out=0x300000, max_len=(100,), base=(0,), lens_dev=0x700000, n_q=1,
+             ws=1 << 30):
+        return lib.nvfp4_decode_step_dev_len(ctypes.byref(d), 0x400000, k, v, q, out, 0, 1, qk._i64(base),
+                                             qk._i64(max_len), lens_dev, n_q, 24, 0.0625, 0x500000, ws, None)
+    assert call(lens_dev=0) == qk.EINVAL                  # device lengths required
+    assert call(lens_dev=0x700004) == qk.EINVAL           # 8-byte alignment
+    assert call(k=0) == qk.EINVAL                         # only one of k_new / v_new
+    assert call(q=0) == qk.EINVAL
+    assert call(max_len=(0,)) == qk.ERANGE                # the bound must hold n_q tokens
+    assert call(base=(950,)) == qk.ERANGE                 # bound past capacity
+    assert call(ws=16) == qk.EWORKSPACE
+    assert lib.nvfp4_decode_step_dev_len(ctypes.byref(d), 0x400000, a, a, 0x200000, 0x300000, 0, 1, qk._i64([0]),
+                                         None, 0x700000, 1, 24, 0.0625, 0x500000, 1 << 30, None) == qk.EINVAL
 
 
 def test_split_plan_last_unit_holds_new_rows(lib):

@@ -169,6 +169,117 @@ def test_decode_step_equals_append_then_decode(qk, shape):
     _check_decode(w, ref, out_b)
 
 
+def _spaced_pool(qk, w, max_len):
+    """A pool in which sequence b owns slots [base[b], base[b] + max_len[b]): room to grow."""
+    base = [int(x) for x in np.concatenate([[0], np.cumsum(max_len)[:-1]])]
+    return qk.KVPool(w.num_kv_heads, w.head_dim, int(sum(max_len)), device="cuda"), base
+
+
+def _seq_rows(t, w, lo, hi):
+    """Rows [lo[b], hi[b]) of every sequence b of w's row tensor, concatenated over b."""
+    return torch.cat([t[w.seq_base[b] + lo[b]:w.seq_base[b] + hi[b]] for b in range(w.batch)]).contiguous()
+
+
+def _assert_seq_slots_equal(pool, base, ref, w):
+    for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
+        got = getattr(pool, name).cpu().numpy()
+        exp = getattr(ref.cache, name)
+        for b in range(w.batch):
+            L = w.seq_lens[b]
+            assert np.array_equal(got[:, base[b]:base[b] + L], exp[:, w.seq_base[b]:w.seq_base[b] + L]), (name, b)
+
+
+DEV_LEN_CASES = [
+    (dict(seq_lens=(512,), num_kv_heads=1, num_q_heads=4, head_dim=128, n_q=1), 0),          # bound = length
+    (dict(seq_lens=(1000, 77, 3), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=1), 700),
+    (dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=4), 3000),   # 24 rows
+    (dict(seq_lens=(963,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6, outlier_frac=0.02), 5000),
+    (dict(seq_lens=(6, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6), 100000),     # nearly all units empty
+    (dict(seq_lens=(9, 20), num_kv_heads=1, num_q_heads=4, head_dim=256, n_q=1), 60000),      # one row tile, same
+]
+
+
+@pytest.mark.parametrize("shape,extra", DEV_LEN_CASES)
+def test_decode_step_device_lengths(qk, shape, extra):
+    """nvfp4_decode_step_dev_len with lengths in device memory and an upper bound max_len:
+    the step's rows land in the same bytes as the oracle's, the output passes the oracle."""
+    w = workloads.small(**shape)
+    say("decode step, device lengths", shape, "bound +", extra)
+    ref = OracleRun(w)
+    max_len = [L + extra for L in w.seq_lens]
+    pool, base = _spaced_pool(qk, w, max_len)
+    kd, vd = ref.k.cuda(), ref.v.cuda()
+    g = qk.calibrate(pool, kd, vd, list(w.seq_lens))
+    lens = list(w.seq_lens)
+    pre = [L - w.n_q for L in lens]
+    zero = [0] * w.batch
+    qk.append(pool, _seq_rows(kd, w, zero, pre), _seq_rows(vd, w, zero, pre), g, base, zero, pre)
+    lens_dev = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    out = qk.decode_step_dev_len(pool, g, _seq_rows(kd, w, pre, lens), _seq_rows(vd, w, pre, lens), ref.q.cuda(),
+                                 base, max_len, lens_dev, w.sm_scale)
+    torch.cuda.synchronize()
+    _assert_seq_slots_equal(pool, base, ref, w)
+    _check_decode(w, ref, out)
+
+
+@pytest.mark.parametrize("n_q", [1, 4])
+def test_decode_step_device_lengths_graph_replay(qk, n_q):
+    """One HIP graph of the device-length step, captured once and replayed over four decode
+    steps while the sequences grow by n_q tokens per step (new q, k_new, v_new and lengths
+    written into the same buffers between replays): every replay passes the oracle at its
+    lengths, the pool matches the oracle's bytes at the end, and replaying the last step
+    again gives identical output bits."""
+    w = workloads.small(seq_lens=(1500, 333), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=n_q)
+    say("graph replay, device lengths, n_q", n_q)
+    ref = OracleRun(w)
+    steps = 4
+    lens = list(w.seq_lens)
+    max_len = [L + 64 for L in lens]
+    pool, base = _spaced_pool(qk, w, max_len)
+    kd, vd = ref.k.cuda(), ref.v.cuda()
+    g = qk.calibrate(pool, kd, vd, lens)
+    start = [L - steps * n_q for L in lens]
+    zero = [0] * w.batch
+    qk.append(pool, _seq_rows(kd, w, zero, start), _seq_rows(vd, w, zero, start), g, base, zero, start)
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    q_buf = torch.zeros((B, n_q, Hq, D), dtype=torch.bfloat16, device="cuda")
+    k_buf = torch.zeros((B * n_q, w.num_kv_heads, D), dtype=torch.bfloat16, device="cuda")
+    v_buf = torch.zeros_like(k_buf)
+    lens_dev = torch.tensor(start, dtype=torch.int64, device="cuda")
+    out_buf = torch.zeros((B, n_q, Hq, D), dtype=torch.float32, device="cuda")
+    ws = qk.alloc_workspace(pool, max_len, n_q, Hq)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            qk.decode_step_dev_len(pool, g, k_buf, v_buf, q_buf, base, max_len, lens_dev, w.sm_scale, out=out_buf,
+                                   workspace=ws)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(77)
+    tol = TOL_REL * ref.vmax()
+    for s in range(steps):
+        now = [st + (s + 1) * n_q for st in start]
+        q_s = torch.randn((B, n_q, Hq, D), generator=gen).to(torch.bfloat16)
+        q_buf.copy_(q_s)
+        k_buf.copy_(_seq_rows(kd, w, [L - n_q for L in now], now))
+        v_buf.copy_(_seq_rows(vd, w, [L - n_q for L in now], now))
+        lens_dev.copy_(torch.tensor(now, dtype=torch.int64))
+        graph.replay()
+        torch.cuda.synchronize()
+        exp = oracle.attention(ref.cache, ref.g, workloads.as_u16(q_s), w.seq_base, now, n_q, w.sm_scale)
+        err = max_err(out_buf.cpu().numpy(), exp)
+        say(f"  step {s} lengths {now}: max err {err:.3e}  tol {tol:.3e}")
+        assert err <= tol
+    _assert_seq_slots_equal(pool, base, ref, w)
+    first = out_buf.clone()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(first, out_buf)
+
+
 def test_decode_deterministic_and_partial_combine_split(qk):
     w = workloads.small(seq_lens=(5000, 1234), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=6)
     say("determinism")
