@@ -63,7 +63,7 @@ extern "C" {
 #define NVFP4_OUT_BF16 1
 
 #define NVFP4_MAX_SEQS 8         /* active sequences per call                         */
-#define NVFP4_MAX_ROWS 64        /* GQA group x query tokens sharing one KV head      */
+#define NVFP4_MAX_ROWS 128       /* GQA group x query tokens sharing one KV head      */
 
 /* The caller-owned pool. head_dim must be 128 or 256; num_kv_heads >= 1;
  * capacity >= 1 token slots per head plane, and capacity * head_dim / 2 (one
@@ -123,9 +123,12 @@ size_t nvfp4_decode_attn_workspace_bytes(const nvfp4_kv_cache *cache, int32_t nu
  *   seq_base: host int64 [num_seqs]
  *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
  *   out = softmax(sm_scale * q . k_hat) . v_hat, computed with fp32 accumulation.
+ *   Up to 64 query rows per KV head ((num_q_heads/num_kv_heads) * n_q) are served by one
+ *   pass over the cache; 65..128 rows (wide draft windows, e.g. n_q = 16 at a GQA group
+ *   of 6) by two passes over balanced halves of the rows, so the KV bytes are read twice.
  * Errors: EINVAL (pointers, out_dtype, n_q < 1, non-finite sm_scale),
  *         EUNSUPPORTED (head_dim, num_q_heads % num_kv_heads != 0, num_seqs > 8,
- *         (num_q_heads/num_kv_heads) * n_q > 64), ERANGE (seq_len < n_q, slots past
+ *         (num_q_heads/num_kv_heads) * n_q > 128), ERANGE (seq_len < n_q, slots past
  *         capacity), EWORKSPACE (workspace_bytes below the size query). */
 int nvfp4_decode_attn(const nvfp4_kv_cache *cache, const float *global_scale, const void *q,
                       void *out, int32_t out_dtype, int32_t num_seqs, const int64_t *seq_base,

@@ -90,7 +90,11 @@ int make_plan(const nvfp4_kv_cache *c, int32_t num_seqs, const int64_t *seq_base
     pl.G = G;
     pl.n_q = n_q;
     pl.R = G * n_q;
-    pl.NT = (pl.R + 15) / 16;
+    // Up to 64 rows per KV head go through the decode kernels in one pass; more are cut into
+    // balanced chunks of whole row tiles, one partial launch each over the same units.
+    const int chunks = (pl.R + nvfp4::kMaxRows - 1) / nvfp4::kMaxRows;
+    pl.chunk_rows = ((pl.R + chunks - 1) / chunks + 15) / 16 * 16;
+    pl.NT = (std::min(pl.chunk_rows, pl.R) + 15) / 16;
     pl.D = c->head_dim;
     // Fill every CU once, with as many workgroups as the kernel for NT row tiles keeps
     // resident. Splits go greedily to the sequence whose units are currently longest,
@@ -166,6 +170,8 @@ void fill_decode(nvfp4::DecodeParams &dp, const nvfp4::SplitPlan &pl, const nvfp
     dp.G = pl.G;
     dp.n_q = pl.n_q;
     dp.R = pl.R;
+    dp.row0 = 0;
+    dp.Rc = std::min(pl.chunk_rows, pl.R);
     for (int b = 0; b < nvfp4::kMaxSeqs; ++b) {
         dp.seq_base[b] = (b < pl.B && seq_base) ? seq_base[b] : 0;
         dp.seq_len[b] = (b < pl.B) ? seq_len[b] : 0;
@@ -174,6 +180,19 @@ void fill_decode(nvfp4::DecodeParams &dp, const nvfp4::SplitPlan &pl, const nvfp
         dp.unit_base[b] = pl.unit_base[b];
     }
     dp.units = pl.units;
+}
+
+// The partial kernel over every row chunk (one launch per chunk, the same units); only the
+// first launch stores the step's new rows, which the later ones then read.
+hipError_t launch_partials(nvfp4::DecodeParams dp, const nvfp4::SplitPlan &pl, hipStream_t s) {
+    for (int r0 = 0; r0 < pl.R; r0 += pl.chunk_rows) {
+        dp.row0 = r0;
+        dp.Rc = std::min(pl.chunk_rows, pl.R - r0);
+        hipError_t e = nvfp4::launch_decode_partial(dp, pl.D, (dp.Rc + 15) / 16, s);
+        if (e != hipSuccess) return e;
+        dp.k_new = dp.v_new = nullptr;
+    }
+    return hipSuccess;
 }
 
 int check_decode_common(const float *global_scale, void *workspace, size_t workspace_bytes,
@@ -283,8 +302,7 @@ int nvfp4_decode_attn_partial(const nvfp4_kv_cache *cache, const float *global_s
     if (!std::isfinite(sm_scale)) return fail(NVFP4_EINVAL, "sm_scale must be finite");
     nvfp4::DecodeParams dp;
     fill_decode(dp, pl, cache, global_scale, q, seq_base, seq_len, sm_scale, workspace);
-    return hip_status(nvfp4::launch_decode_partial(dp, pl.D, pl.NT, static_cast<hipStream_t>(stream)),
-                      "decode partial launch");
+    return hip_status(launch_partials(dp, pl, static_cast<hipStream_t>(stream)), "decode partial launch");
 }
 
 int nvfp4_decode_attn_combine(const nvfp4_kv_cache *cache, const float *global_scale, void *out, int32_t out_dtype,
@@ -329,7 +347,7 @@ int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, co
     dp.out = out;
     dp.out_bf16 = out_dtype == NVFP4_OUT_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = nvfp4::launch_decode_partial(dp, pl.D, pl.NT, s);
+    hipError_t e = launch_partials(dp, pl, s);
     if (e != hipSuccess) return hip_status(e, "decode partial launch");
     return hip_status(nvfp4::launch_decode_combine(dp, pl.D, s), "decode combine launch");
 }
@@ -366,7 +384,7 @@ int nvfp4_decode_step_dev_len(const nvfp4_kv_cache *cache, const float *global_s
     dp.out = out;
     dp.out_bf16 = out_dtype == NVFP4_OUT_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = nvfp4::launch_decode_partial(dp, pl.D, pl.NT, s);
+    hipError_t e = launch_partials(dp, pl, s);
     if (e != hipSuccess) return hip_status(e, "decode partial launch");
     return hip_status(nvfp4::launch_decode_combine(dp, pl.D, s), "decode combine launch");
 }
@@ -391,7 +409,7 @@ int nvfp4_decode_attn(const nvfp4_kv_cache *cache, const float *global_scale, co
     dp.out = out;
     dp.out_bf16 = out_dtype == NVFP4_OUT_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = nvfp4::launch_decode_partial(dp, pl.D, pl.NT, s);
+    hipError_t e = launch_partials(dp, pl, s);
     if (e != hipSuccess) return hip_status(e, "decode partial launch");
     return hip_status(nvfp4::launch_decode_combine(dp, pl.D, s), "decode combine launch");
 }

@@ -303,7 +303,8 @@ void decode_partial_kernel(DecodeParams p) {
     // block loop on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    const int R = p.R, G = p.G;
+    // R: this launch's rows [row0, row0 + R) of the KV head's Rt = G n_q rows
+    const int R = p.Rc, G = p.G, Rt = p.R, row0 = p.row0;
     const int64_t base = p.seq_base[b];
     const uint32_t code_bytes = (uint32_t)(p.cap * (D / 2)), scale_bytes = (uint32_t)(p.cap * (D / 16));
     const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * code_bytes, code_bytes);
@@ -344,7 +345,7 @@ void decode_partial_kernel(DecodeParams p) {
     for (int rt = 0; rt < NT; ++rt) {
         const int row = 16 * rt + n;
         cexp[rt] = sm_c[row];
-        qi[rt] = row < R ? row / G : p.n_q;          // padded rows see every key (their q is 0)
+        qi[rt] = row < R ? (row0 + row) / G : p.n_q;  // padded rows see every key (their q is 0)
     }
 
     State<D, NT> st;
@@ -414,7 +415,7 @@ void decode_partial_kernel(DecodeParams p) {
         }
     }
     float(*buf)[16][LD::STRIDE] = reinterpret_cast<float(*)[16][LD::STRIDE]>(lds);
-    float *ws_o = p.ws_o + (int64_t)u * R * D;
+    float *ws_o = p.ws_o + ((int64_t)u * Rt + row0) * D;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
         // Only rows below R are stored. Lane n's D/16 values sit at a stride of D/16 floats
@@ -456,8 +457,8 @@ void decode_partial_kernel(DecodeParams p) {
             const float mw = sm_m[w][row];
             if (mw != -INFINITY) Ls += exp2f(mw - M) * sm_l[w][row];
         }
-        p.ws_m[(int64_t)u * R + row] = M;
-        p.ws_l[(int64_t)u * R + row] = Ls;
+        p.ws_m[(int64_t)u * Rt + row0 + row] = M;
+        p.ws_l[(int64_t)u * Rt + row0 + row] = Ls;
     }
 }
 

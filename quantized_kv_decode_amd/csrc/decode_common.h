@@ -165,9 +165,10 @@ __device__ inline void q_load(const DecodeParams &p, int b, int kh, int rt, int 
     constexpr int QD = D / 4;
     const int n = lane & 15, g = lane >> 4;
     const int row = 16 * rt + n;
-    if (row < p.R) {
-        const int i = row / p.G;
-        const int h = kh * p.G + (row - i * p.G);
+    if (row < p.Rc) {
+        const int grow = p.row0 + row;                 // row of the KV head's G n_q rows
+        const int i = grow / p.G;
+        const int h = kh * p.G + (grow - i * p.G);
         const uint16_t *qr = p.q + (((int64_t)b * p.n_q + i) * p.Hq + h) * D + QD * g;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -208,7 +209,7 @@ __device__ inline void q_store(const DecodeParams &p, int b, int kh, int rt, int
     }
     if (g == 0) {
         const float gk = p.gscale[(b * p.Hkv + kh) * 2 + 0];
-        sm_c[row] = row < p.R ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
+        sm_c[row] = row < p.Rc ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
     }
 }
 

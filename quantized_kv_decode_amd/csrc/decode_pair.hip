@@ -144,7 +144,8 @@ void decode_pair_kernel(DecodeParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = wave >> 1, w = wave & 1;
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-    const int R = p.R, G = p.G;
+    // R: this launch's rows [row0, row0 + R) of the KV head's Rt = G n_q rows
+    const int R = p.Rc, G = p.G, Rt = p.R, row0 = p.row0;
     const uint32_t code_bytes = (uint32_t)(p.cap * (D / 2)), scale_bytes = (uint32_t)(p.cap * (D / 16));
     const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * code_bytes, code_bytes);
     const rsrc_t ks = plane_rsrc(p.ks + (int64_t)kh * scale_bytes, scale_bytes);
@@ -186,7 +187,7 @@ void decode_pair_kernel(DecodeParams p) {
     for (int rt = 0; rt < NT; ++rt) {
         const int row = 16 * rt + n;
         cexp[rt] = sm_c[row];
-        qi[rt] = row < R ? row / G : p.n_q;          // padded rows see every key (their q is 0)
+        qi[rt] = row < R ? (row0 + row) / G : p.n_q;  // padded rows see every key (their q is 0)
     }
 
     float4_t acc[NT][HT];    // rows 16 rt + 4 g + i, d = EPL n + HT w + t
@@ -362,7 +363,7 @@ void decode_pair_kernel(DecodeParams p) {
         }
     }
     float4_t(*mbuf)[HT][64] = reinterpret_cast<float4_t(*)[HT][64]>(big);   // [role][t][lane]
-    float *ws_o = p.ws_o + (int64_t)u * R * D;
+    float *ws_o = p.ws_o + ((int64_t)u * Rt + row0) * D;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
         if (pair == 1) {
@@ -394,8 +395,8 @@ void decode_pair_kernel(DecodeParams p) {
         float Ls = 0.f;
         if (m0 != -INFINITY) Ls += exp2f(m0 - M) * sm_l[0][row];
         if (m1 != -INFINITY) Ls += exp2f(m1 - M) * sm_l[1][row];
-        p.ws_m[(int64_t)u * R + row] = M;
-        p.ws_l[(int64_t)u * R + row] = Ls;
+        p.ws_m[(int64_t)u * Rt + row0 + row] = M;
+        p.ws_l[(int64_t)u * Rt + row0 + row] = Ls;
     }
 }
 

@@ -25,6 +25,7 @@ constexpr int decode_wgs_per_cu(int NT) { return NT == 2 ? 3 : 2; }
 // split.
 struct SplitPlan {
     int32_t B, Hkv, Hq, G, n_q, R, NT, D;
+    int32_t chunk_rows;                  // rows per partial launch (the last may have fewer)
     int32_t n_split[kMaxSeqs];
     int32_t split_len[kMaxSeqs];
     int32_t unit_base[kMaxSeqs];
@@ -44,7 +45,8 @@ struct DecodeParams {
     void *out;
     int32_t out_bf16;
     float sm_scale;
-    int32_t B, Hkv, Hq, G, n_q, R;
+    int32_t B, Hkv, Hq, G, n_q, R;       // R = G n_q rows per KV head (workspace stride)
+    int32_t row0, Rc;                    // this partial launch's rows: [row0, row0 + Rc), Rc <= 64
     int64_t seq_base[kMaxSeqs];
     int64_t seq_len[kMaxSeqs];
     int32_t n_split[kMaxSeqs];

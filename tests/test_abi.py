@@ -78,7 +78,7 @@ def test_decode_validation_codes(lib):
     assert _call_decode(qk, lib, _desc(qk, H=0)) == qk.EINVAL
     assert _call_decode(qk, lib, _desc(qk, addr=0x100008)) == qk.EINVAL          # unaligned plane
     assert _call_decode(qk, lib, d, Hq=25) == qk.EUNSUPPORTED                      # Hq % Hkv
-    assert _call_decode(qk, lib, d, n_q=11) == qk.EUNSUPPORTED                     # 6 x 11 rows > 64
+    assert _call_decode(qk, lib, d, n_q=22) == qk.EUNSUPPORTED                     # 6 x 22 rows > 128
     assert _call_decode(qk, lib, d, n_q=0) == qk.EINVAL
     assert _call_decode(qk, lib, d, B=0) == qk.EINVAL
     assert _call_decode(qk, lib, d, B=9, lens=[10] * 9, base=[0] * 9) == qk.EUNSUPPORTED
@@ -164,6 +164,20 @@ def test_decode_step_dev_len_validation_codes(lib):
     assert call(ws=16) == qk.EWORKSPACE
     assert lib.nvfp4_decode_step_dev_len(ctypes.byref(d), 0x400000, a, a, 0x200000, 0x300000, 0, 1, qk._i64([0]),
                                          None, 0x700000, 1, 24, 0.0625, 0x500000, 1 << 30, None) == qk.EINVAL
+
+
+def test_wide_row_counts_plan_like_their_chunks(lib):
+    """65..128 rows per KV head run as two balanced row chunks over one split plan: 96 rows
+    (n_q = 16, G = 6) are planned as 48-row (three-tile) passes, 72 rows as 48 + 24, and the
+    workspace holds every row of every unit."""
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk, cap=10 ** 6)
+    al = lambda x: (x + 255) // 256 * 256
+    ws = lambda L, n_q: lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([L]), n_q, 24)
+    units = 256 * 2                                      # two workgroups per CU at three row tiles
+    for n_q in (16, 12):
+        R = 6 * n_q
+        assert ws(10 ** 6, n_q) == al(units * R * 256 * 4) + 2 * al(units * R * 4)
 
 
 def test_split_plan_last_unit_holds_new_rows(lib):

@@ -101,6 +101,11 @@ DECODE_SHAPES = [
     dict(seq_lens=(2050,), num_kv_heads=2, num_q_heads=2, head_dim=128, n_q=5),                            # G = 1
     dict(seq_lens=(333, 100), num_kv_heads=1, num_q_heads=16, head_dim=256, n_q=4),                       # 64 rows
     dict(seq_lens=(257,), num_kv_heads=1, num_q_heads=8, head_dim=128, n_q=6),                            # 48 rows
+    # wide draft windows: two row chunks over one split plan
+    dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=16),   # 96 rows: 48 + 48
+    dict(seq_lens=(900, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=12, v_dist="laplace"),  # 72: 48 + 24
+    dict(seq_lens=(600,), num_kv_heads=1, num_q_heads=16, head_dim=128, n_q=8),         # 128 rows: 64 + 64
+    dict(seq_lens=(17, 90), num_kv_heads=1, num_q_heads=5, head_dim=256, n_q=15),      # 75 rows, lengths < 2 blocks
 ]
 
 
@@ -196,6 +201,7 @@ DEV_LEN_CASES = [
     (dict(seq_lens=(963,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6, outlier_frac=0.02), 5000),
     (dict(seq_lens=(6, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6), 100000),     # nearly all units empty
     (dict(seq_lens=(9, 20), num_kv_heads=1, num_q_heads=4, head_dim=256, n_q=1), 60000),      # one row tile, same
+    (dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=16), 2000),  # 96 rows, two chunks
 ]
 
 
@@ -370,7 +376,7 @@ def _sample_rows(w, per_head_rows):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,per_head", [("tiny", None), ("decode_27b", None), ("mtp_verify", 3),
-                                           ("long_agentic", 1)])
+                                           ("long_agentic", 1), ("dflash_verify", 3)])
 def test_full_workload(qk, name, per_head):
     w = workloads.get(name)
     say("full workload", name, w.seq_lens)

@@ -122,6 +122,11 @@ WORKLOADS = {
     "append_max_context": Workload(
         "append_max_context", 5, (600000,), 4, 24, 256, 1, append_rows=8192,
         description="append an 8192-row prefill chunk into a 600000-token cache, then decode over all 600000"),
+    # not one of the five configurations: a wide draft window (DFlash-style, 1 + 15 drafts),
+    # 96 query rows per KV head, which the decode path serves in two row chunks
+    "dflash_verify": Workload(
+        "dflash_verify", 6, (131072,), 4, 24, 256, 16, outlier_frac=0.02,
+        description="wide draft verify: 1 x 131072, 16 query tokens (1 + 15 drafts) causal, 2% channels x20"),
 }
 
 ORDER = ["tiny", "decode_27b", "mtp_verify", "long_agentic", "append_max_context"]
