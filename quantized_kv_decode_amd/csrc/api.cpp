@@ -96,10 +96,9 @@ int make_plan(const nvfp4_kv_cache *c, int32_t num_seqs, const int64_t *seq_base
     pl.chunk_rows = ((pl.R + chunks - 1) / chunks + 15) / 16 * 16;
     pl.NT = (std::min(pl.chunk_rows, pl.R) + 15) / 16;
     pl.D = c->head_dim;
-    // Fill every CU once, with as many workgroups as the kernel for NT row tiles keeps
-    // resident. Splits go greedily to the sequence whose units are currently longest,
-    // so ragged batches get near-equal units.
-    const int64_t slots = std::max<int64_t>((int64_t)nvfp4::kCUs * nvfp4::decode_wgs_per_cu(pl.NT),
+    // Fill every CU with decode_units_per_cu(NT) units. Splits go greedily to the sequence
+    // whose units are currently longest, so ragged batches get near-equal units.
+    const int64_t slots = std::max<int64_t>((int64_t)nvfp4::kCUs * nvfp4::decode_units_per_cu(pl.NT),
                                             (int64_t)num_seqs * pl.Hkv);
     int64_t nsp[nvfp4::kMaxSeqs];
     for (int b = 0; b < num_seqs; ++b) nsp[b] = 1;

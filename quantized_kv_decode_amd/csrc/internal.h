@@ -14,9 +14,13 @@ constexpr int kWaves = 4;            // waves per decode workgroup (256 threads)
 constexpr int kCUs = 256;            // compute units the split plan fills (MI355X)
 
 // Resident decode workgroups (256 threads) per CU that the partial kernel for NT row
-// tiles is built for: its waves per SIMD, set by its register budget. The split
-// planner fills that many per CU.
+// tiles is built for: its waves per SIMD, set by its register budget.
 constexpr int decode_wgs_per_cu(int NT) { return NT == 2 ? 3 : 2; }
+// Units the split planner gives each CU. One row tile: one unit per CU, although two such
+// workgroups fit: half as many, twice as long units pay the per-unit start and merge half
+// as often (decode at 2 x 32k tokens: partial 21.6 -> 20.2 us; 600k: 123.1 -> 121.7 us).
+// Two to four row tiles: as many as stay resident (fewer was measured slower).
+constexpr int decode_units_per_cu(int NT) { return NT == 1 ? 1 : decode_wgs_per_cu(NT); }
 
 // Split-K plan: sequence b is cut into n_split[b] units of split_len[b] tokens
 // (a multiple of kBlockTokens) for each KV head; the last unit ends at the
