@@ -63,7 +63,7 @@ extern "C" {
 #define NVFP4_OUT_BF16 1
 
 #define NVFP4_MAX_SEQS 8         /* active sequences per call                         */
-#define NVFP4_MAX_ROWS 128       /* GQA group x query tokens sharing one KV head      */
+#define NVFP4_MAX_ROWS 8192      /* GQA group x query tokens sharing one KV head      */
 
 /* The caller-owned pool. head_dim must be 128 or 256; num_kv_heads >= 1;
  * capacity >= 1 token slots per head plane, and capacity * head_dim / 2 (one
@@ -125,10 +125,12 @@ size_t nvfp4_decode_attn_workspace_bytes(const nvfp4_kv_cache *cache, int32_t nu
  *   out = softmax(sm_scale * q . k_hat) . v_hat, computed with fp32 accumulation.
  *   Up to 64 query rows per KV head ((num_q_heads/num_kv_heads) * n_q) are served by one
  *   pass over the cache; 65..128 rows (wide draft windows, e.g. n_q = 16 at a GQA group
- *   of 6) by two passes over balanced halves of the rows, so the KV bytes are read twice.
+ *   of 6) by two passes over balanced halves of the rows, so the KV bytes are read twice;
+ *   129..8192 rows (a prefill chunk attending to the cache and, causally, to itself) by
+ *   row chunks of at most 64 side by side, each skipping the keys its rows cannot see.
  * Errors: EINVAL (pointers, out_dtype, n_q < 1, non-finite sm_scale),
  *         EUNSUPPORTED (head_dim, num_q_heads % num_kv_heads != 0, num_seqs > 8,
- *         (num_q_heads/num_kv_heads) * n_q > 128), ERANGE (seq_len < n_q, slots past
+ *         (num_q_heads/num_kv_heads) * n_q > 8192), ERANGE (seq_len < n_q, slots past
  *         capacity), EWORKSPACE (workspace_bytes below the size query). */
 int nvfp4_decode_attn(const nvfp4_kv_cache *cache, const float *global_scale, const void *q,
                       void *out, int32_t out_dtype, int32_t num_seqs, const int64_t *seq_base,
@@ -146,7 +148,9 @@ int nvfp4_decode_attn(const nvfp4_kv_cache *cache, const float *global_scale, co
  * the workgroups that read them, so the step is two kernel launches instead of three.
  *   k_new, v_new: device bf16 [num_seqs * n_q][num_kv_heads][head_dim], sequence 0's
  *                 n_q rows first; row r of sequence b goes to slot
- *                 seq_base[b] + seq_len[b] - n_q + r.
+ *                 seq_base[b] + seq_len[b] - n_q + r. (Above 128 query rows per KV head
+ *                 -- a prefill chunk -- the rows are stored by the append kernel first:
+ *                 three launches.)
  *   Other arguments, the workspace and the errors as for nvfp4_decode_attn (EINVAL
  *   also for null or unaligned k_new / v_new). */
 int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, const void *k_new,
@@ -173,7 +177,8 @@ int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, co
  *                (no access outside the sequence's slots; the result is then meaningless).
  *   k_new, v_new: as for nvfp4_decode_step, or both null: attention only, no append.
  *   Other arguments, the workspace and the errors as for nvfp4_decode_step (EINVAL also
- *   for a null or unaligned seq_len_dev, or only one of k_new / v_new null). */
+ *   for a null or unaligned seq_len_dev, or only one of k_new / v_new null; EUNSUPPORTED
+ *   for k_new with more than 128 query rows per KV head: append those rows first). */
 int nvfp4_decode_step_dev_len(const nvfp4_kv_cache *cache, const float *global_scale, const void *k_new,
                               const void *v_new, const void *q, void *out, int32_t out_dtype,
                               int32_t num_seqs, const int64_t *seq_base, const int64_t *max_len,

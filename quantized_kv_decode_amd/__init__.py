@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4kv.so")
 
 OK, EINVAL, EUNSUPPORTED, ERANGE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 OUT_F32, OUT_BF16 = 0, 1
-MAX_SEQS, MAX_ROWS = 8, 128
+MAX_SEQS, MAX_ROWS = 8, 8192
 
 _ERR_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ERANGE: "ERANGE",
               EWORKSPACE: "EWORKSPACE", EHIP: "EHIP"}

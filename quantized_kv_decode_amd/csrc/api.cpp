@@ -91,14 +91,18 @@ int make_plan(const nvfp4_kv_cache *c, int32_t num_seqs, const int64_t *seq_base
     pl.n_q = n_q;
     pl.R = G * n_q;
     // Up to 64 rows per KV head go through the decode kernels in one pass; more are cut into
-    // balanced chunks of whole row tiles, one partial launch each over the same units.
-    const int chunks = (pl.R + nvfp4::kMaxRows - 1) / nvfp4::kMaxRows;
-    pl.chunk_rows = ((pl.R + chunks - 1) / chunks + 15) / 16 * 16;
+    // balanced chunks of whole row tiles over the same units: two chunks (up to 128 rows,
+    // wide draft windows) as two launches in a row, more (prefill chunks) side by side as
+    // grid y of one launch, with correspondingly fewer units.
+    pl.chunks = (pl.R + nvfp4::kMaxRows - 1) / nvfp4::kMaxRows;
+    pl.chunk_rows = ((pl.R + pl.chunks - 1) / pl.chunks + 15) / 16 * 16;
+    pl.chunks = (pl.R + pl.chunk_rows - 1) / pl.chunk_rows;
     pl.NT = (std::min(pl.chunk_rows, pl.R) + 15) / 16;
     pl.D = c->head_dim;
     // Fill every CU with decode_units_per_cu(NT) units. Splits go greedily to the sequence
     // whose units are currently longest, so ragged batches get near-equal units.
-    const int64_t slots = std::max<int64_t>((int64_t)nvfp4::kCUs * nvfp4::decode_units_per_cu(pl.NT),
+    const int64_t grid_y = pl.chunks > 2 ? pl.chunks : 1;
+    const int64_t slots = std::max<int64_t>((int64_t)nvfp4::kCUs * nvfp4::decode_units_per_cu(pl.NT) / grid_y,
                                             (int64_t)num_seqs * pl.Hkv);
     int64_t nsp[nvfp4::kMaxSeqs];
     for (int b = 0; b < num_seqs; ++b) nsp[b] = 1;
@@ -171,6 +175,7 @@ void fill_decode(nvfp4::DecodeParams &dp, const nvfp4::SplitPlan &pl, const nvfp
     dp.R = pl.R;
     dp.row0 = 0;
     dp.Rc = std::min(pl.chunk_rows, pl.R);
+    dp.grid_y = 1;
     for (int b = 0; b < nvfp4::kMaxSeqs; ++b) {
         dp.seq_base[b] = (b < pl.B && seq_base) ? seq_base[b] : 0;
         dp.seq_len[b] = (b < pl.B) ? seq_len[b] : 0;
@@ -181,9 +186,17 @@ void fill_decode(nvfp4::DecodeParams &dp, const nvfp4::SplitPlan &pl, const nvfp
     dp.units = pl.units;
 }
 
-// The partial kernel over every row chunk (one launch per chunk, the same units); only the
-// first launch stores the step's new rows, which the later ones then read.
+// The partial kernel over every row chunk (the same units). Up to two chunks: one launch
+// each, and only the first stores the step's new rows, which the second then reads. More:
+// one launch with the chunks on grid y (the caller has stored the new rows before).
 hipError_t launch_partials(nvfp4::DecodeParams dp, const nvfp4::SplitPlan &pl, hipStream_t s) {
+    if (pl.chunks > 2) {
+        dp.row0 = 0;
+        dp.Rc = pl.chunk_rows;
+        dp.grid_y = pl.chunks;
+        dp.k_new = dp.v_new = nullptr;
+        return nvfp4::launch_decode_partial(dp, pl.D, pl.NT, s);
+    }
     for (int r0 = 0; r0 < pl.R; r0 += pl.chunk_rows) {
         dp.row0 = r0;
         dp.Rc = std::min(pl.chunk_rows, pl.R - r0);
@@ -346,6 +359,16 @@ int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, co
     dp.out = out;
     dp.out_bf16 = out_dtype == NVFP4_OUT_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pl.chunks > 2) {
+        // Row chunks side by side all read the new rows: store them first (append kernel).
+        int64_t wp[nvfp4::kMaxSeqs], nn[nvfp4::kMaxSeqs];
+        for (int b = 0; b < num_seqs; ++b) {
+            wp[b] = seq_len[b] - n_q;
+            nn[b] = n_q;
+        }
+        if ((rc = nvfp4_kv_append(cache, k_new, v_new, global_scale, num_seqs, seq_base, wp, nn, stream)))
+            return rc;
+    }
     hipError_t e = launch_partials(dp, pl, s);
     if (e != hipSuccess) return hip_status(e, "decode partial launch");
     return hip_status(nvfp4::launch_decode_combine(dp, pl.D, s), "decode combine launch");
@@ -370,6 +393,9 @@ int nvfp4_decode_step_dev_len(const nvfp4_kv_cache *cache, const float *global_s
         return fail(NVFP4_EINVAL, "k_new and v_new must both be given or both be null");
     if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
         return fail(NVFP4_EINVAL, "k_new and v_new must be 16-byte aligned");
+    if (k_new && pl.chunks > 2)
+        return fail(NVFP4_EUNSUPPORTED, "%d query rows per KV head: with lengths in device memory the step "
+                    "stores its rows itself only up to 128 rows (append first, pass null k_new/v_new)", pl.R);
     if (!aligned16(q)) return fail(NVFP4_EINVAL, "q must be non-null and 16-byte aligned");
     if (!aligned16(out)) return fail(NVFP4_EINVAL, "out must be non-null and 16-byte aligned");
     if (out_dtype != NVFP4_OUT_F32 && out_dtype != NVFP4_OUT_BF16)

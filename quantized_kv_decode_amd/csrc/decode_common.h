@@ -125,6 +125,30 @@ __device__ inline Unit unit_of(const DecodeParams &p, int u) {
     return r;
 }
 
+// The query rows of this workgroup: [row0, row0 + Rc) of the KV head's R = G n_q rows
+// (row = query token x G + head in the group). Row chunks launched side by side take the
+// chunk index from blockIdx.y.
+struct Rows {
+    int row0, Rc;
+};
+
+__device__ inline Rows rows_of(const DecodeParams &p) {
+    const int row0 = p.row0 + (int)blockIdx.y * p.Rc;
+    return Rows{row0, min(p.Rc, p.R - row0)};
+}
+
+// Causal trim: keys past the last one that the workgroup's last query token sees are
+// masked for all its rows, so the unit's range stops there (whole blocks are skipped; the
+// result is unchanged). Matters for long query chunks (prefill).
+__device__ inline void trim_causal(Unit &un, const DecodeParams &p, const Rows &rw) {
+    const int64_t i_last = (rw.row0 + rw.Rc - 1) / p.G;
+    const int64_t kend = un.L - p.n_q + i_last + 1;
+    if (un.t1 > kend) {
+        un.t1 = kend > un.t0 ? kend : un.t0;
+        un.nblk = (int)((un.t1 - un.t0 + kBlockTokens - 1) / kBlockTokens);
+    }
+}
+
 // The n_q rows a decode step appends for (sequence b, KV head kh) before reading
 // them: rows b n_q + r (r < n_q) of k_new / v_new, quantised with the sequence's
 // global scales by the append kernel's group quantiser and stored at slots
@@ -160,13 +184,14 @@ __device__ inline void append_step_rows(const DecodeParams &p, int b, int kh, in
 // MFMA score back into sm_scale * q . k_hat * log2(e) (including the 2^8 of the
 // dequantised K and g_K). Rows past R get zero fragments and factor 0.
 template <int D>
-__device__ inline void q_load(const DecodeParams &p, int b, int kh, int rt, int lane, uint32_t (&w)[D / 8]) {
+__device__ inline void q_load(const DecodeParams &p, const Rows &rw, int b, int kh, int rt, int lane,
+                              uint32_t (&w)[D / 8]) {
     constexpr int KK = D / 32;
     constexpr int QD = D / 4;
     const int n = lane & 15, g = lane >> 4;
     const int row = 16 * rt + n;
-    if (row < p.Rc) {
-        const int grow = p.row0 + row;                 // row of the KV head's G n_q rows
+    if (row < rw.Rc) {
+        const int grow = rw.row0 + row;                // row of the KV head's G n_q rows
         const int i = grow / p.G;
         const int h = kh * p.G + (grow - i * p.G);
         const uint16_t *qr = p.q + (((int64_t)b * p.n_q + i) * p.Hq + h) * D + QD * g;
@@ -182,8 +207,8 @@ __device__ inline void q_load(const DecodeParams &p, int b, int kh, int rt, int 
 }
 
 template <int D>
-__device__ inline void q_store(const DecodeParams &p, int b, int kh, int rt, int lane, const uint32_t (&w)[D / 8],
-                               half8_t *qlds, float *sm_c) {
+__device__ inline void q_store(const DecodeParams &p, const Rows &rw, int b, int kh, int rt, int lane,
+                               const uint32_t (&w)[D / 8], half8_t *qlds, float *sm_c) {
     constexpr int KK = D / 32;
     const int n = lane & 15, g = lane >> 4;
     const int row = 16 * rt + n;
@@ -209,7 +234,7 @@ __device__ inline void q_store(const DecodeParams &p, int b, int kh, int rt, int
     }
     if (g == 0) {
         const float gk = p.gscale[(b * p.Hkv + kh) * 2 + 0];
-        sm_c[row] = row < p.Rc ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
+        sm_c[row] = row < rw.Rc ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
     }
 }
 

@@ -139,13 +139,15 @@ void decode_pair_kernel(DecodeParams p) {
     __shared__ float sm_l[kPairs][kMaxRows];
 
     const int u = blockIdx.x;
-    const Unit un = unit_of<DevLen>(p, u);
+    Unit un = unit_of<DevLen>(p, u);
+    const Rows rw = rows_of(p);
+    trim_causal(un, p, rw);
     const int b = un.b, kh = un.kh, nblk = un.nblk;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = wave >> 1, w = wave & 1;
     const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
     // R: this launch's rows [row0, row0 + R) of the KV head's Rt = G n_q rows
-    const int R = p.Rc, G = p.G, Rt = p.R, row0 = p.row0;
+    const int R = rw.Rc, G = p.G, Rt = p.R, row0 = rw.row0;
     const uint32_t code_bytes = (uint32_t)(p.cap * (D / 2)), scale_bytes = (uint32_t)(p.cap * (D / 16));
     const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * code_bytes, code_bytes);
     const rsrc_t ks = plane_rsrc(p.ks + (int64_t)kh * scale_bytes, scale_bytes);
@@ -157,7 +159,7 @@ void decode_pair_kernel(DecodeParams p) {
     // Q row loads first, then the pair's first block: both latencies overlap, and the Q
     // conversion waits only for Q (vector-memory waits are in order).
     uint32_t qw[D / 8];
-    if (wave < NT) q_load<D>(p, b, kh, wave, lane, qw);
+    if (wave < NT) q_load<D>(p, rw, b, kh, wave, lane, qw);
     // A decode step that appends its own rows: the workgroup of the sequence's last unit
     // (the only one that reads those slots) stores them before issuing any KV load. The
     // workgroup barrier orders the stores before every wave's later loads (workgroup-scope
@@ -179,7 +181,7 @@ void decode_pair_kernel(DecodeParams p) {
         pair_load_k<D>(r, kc, ks, o0);
         pair_load_v<D>(r, vc, vs, o0);
     }
-    if (wave < NT) q_store<D>(p, b, kh, wave, lane, qw, qlds, sm_c);
+    if (wave < NT) q_store<D>(p, rw, b, kh, wave, lane, qw, qlds, sm_c);
     __syncthreads();
     float cexp[NT];
     int qi[NT];
@@ -403,9 +405,9 @@ void decode_pair_kernel(DecodeParams p) {
 template <int D, int NT>
 hipError_t launch_pair_t(const DecodeParams &p, hipStream_t s) {
     if (p.len_dev != nullptr)
-        hipLaunchKernelGGL((decode_pair_kernel<D, NT, true>), dim3(p.units), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((decode_pair_kernel<D, NT, true>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_pair_kernel<D, NT, false>), dim3(p.units), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((decode_pair_kernel<D, NT, false>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

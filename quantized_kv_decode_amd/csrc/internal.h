@@ -29,7 +29,8 @@ constexpr int decode_units_per_cu(int NT) { return NT == 1 ? 1 : decode_wgs_per_
 // split.
 struct SplitPlan {
     int32_t B, Hkv, Hq, G, n_q, R, NT, D;
-    int32_t chunk_rows;                  // rows per partial launch (the last may have fewer)
+    int32_t chunk_rows;                  // rows per row chunk (the last may have fewer)
+    int32_t chunks;                      // row chunks; above 2 they run side by side (grid y)
     int32_t n_split[kMaxSeqs];
     int32_t split_len[kMaxSeqs];
     int32_t unit_base[kMaxSeqs];
@@ -50,7 +51,9 @@ struct DecodeParams {
     int32_t out_bf16;
     float sm_scale;
     int32_t B, Hkv, Hq, G, n_q, R;       // R = G n_q rows per KV head (workspace stride)
-    int32_t row0, Rc;                    // this partial launch's rows: [row0, row0 + Rc), Rc <= 64
+    int32_t row0, Rc;                    // rows of the workgroups with blockIdx.y = y:
+                                         // [row0 + y Rc, min(row0 + (y + 1) Rc, R)), Rc <= 64
+    int32_t grid_y;                      // row chunks run side by side (grid y), >= 1
     int64_t seq_base[kMaxSeqs];
     int64_t seq_len[kMaxSeqs];
     int32_t n_split[kMaxSeqs];

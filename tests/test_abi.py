@@ -78,7 +78,7 @@ def test_decode_validation_codes(lib):
     assert _call_decode(qk, lib, _desc(qk, H=0)) == qk.EINVAL
     assert _call_decode(qk, lib, _desc(qk, addr=0x100008)) == qk.EINVAL          # unaligned plane
     assert _call_decode(qk, lib, d, Hq=25) == qk.EUNSUPPORTED                      # Hq % Hkv
-    assert _call_decode(qk, lib, d, n_q=22) == qk.EUNSUPPORTED                     # 6 x 22 rows > 128
+    assert _call_decode(qk, lib, d, n_q=1400) == qk.EUNSUPPORTED                   # 6 x 1400 rows > 8192
     assert _call_decode(qk, lib, d, n_q=0) == qk.EINVAL
     assert _call_decode(qk, lib, d, B=0) == qk.EINVAL
     assert _call_decode(qk, lib, d, B=9, lens=[10] * 9, base=[0] * 9) == qk.EUNSUPPORTED
@@ -164,6 +164,8 @@ def test_decode_step_dev_len_validation_codes(lib):
     assert call(ws=16) == qk.EWORKSPACE
     assert lib.nvfp4_decode_step_dev_len(ctypes.byref(d), 0x400000, a, a, 0x200000, 0x300000, 0, 1, qk._i64([0]),
                                          None, 0x700000, 1, 24, 0.0625, 0x500000, 1 << 30, None) == qk.EINVAL
+    # above 128 rows per KV head the device-length step does not store rows itself
+    assert call(max_len=(800,), n_q=30) == qk.EUNSUPPORTED
 
 
 def test_wide_row_counts_plan_like_their_chunks(lib):
@@ -178,6 +180,18 @@ def test_wide_row_counts_plan_like_their_chunks(lib):
     for n_q in (16, 12):
         R = 6 * n_q
         assert ws(10 ** 6, n_q) == al(units * R * 256 * 4) + 2 * al(units * R * 4)
+
+
+def test_prefill_rows_plan_fewer_units(lib):
+    """More than two row chunks run side by side (grid y), so the planner makes
+    proportionally fewer units: 1024 query tokens at G = 6 are 6144 rows = 96 chunks of 64,
+    and 512 / 96 = 5 unit slots fall below one unit per (sequence, KV head): 4 units."""
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk, cap=10 ** 6)
+    al = lambda x: (x + 255) // 256 * 256
+    R = 6 * 1024
+    got = lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([40000]), 1024, 24)
+    assert got == al(4 * R * 256 * 4) + 2 * al(4 * R * 4)
 
 
 def test_split_plan_last_unit_holds_new_rows(lib):

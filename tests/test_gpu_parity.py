@@ -106,6 +106,10 @@ DECODE_SHAPES = [
     dict(seq_lens=(900, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=12, v_dist="laplace"),  # 72: 48 + 24
     dict(seq_lens=(600,), num_kv_heads=1, num_q_heads=16, head_dim=128, n_q=8),         # 128 rows: 64 + 64
     dict(seq_lens=(17, 90), num_kv_heads=1, num_q_heads=5, head_dim=256, n_q=15),      # 75 rows, lengths < 2 blocks
+    # prefill chunks: many row chunks side by side, each skipping keys its rows cannot see
+    dict(seq_lens=(600,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=64),        # 384 rows: 6 chunks
+    dict(seq_lens=(300, 1000), num_kv_heads=2, num_q_heads=8, head_dim=128, n_q=100),  # 400 rows, ragged
+    dict(seq_lens=(2100,), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=256, v_dist="laplace"),  # 1536 rows
 ]
 
 

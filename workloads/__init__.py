@@ -127,6 +127,11 @@ WORKLOADS = {
     "dflash_verify": Workload(
         "dflash_verify", 6, (131072,), 4, 24, 256, 16, outlier_frac=0.02,
         description="wide draft verify: 1 x 131072, 16 query tokens (1 + 15 drafts) causal, 2% channels x20"),
+    # not one of the five configurations: chunked prefill, a 1024-token chunk appended and
+    # attending (causally among itself) over a 32768-token context, 6144 query rows per KV head
+    "prefill_chunk": Workload(
+        "prefill_chunk", 7, (32768,), 4, 24, 256, 1024,
+        description="chunked prefill: a 1024-token chunk ending a 32768-token context, causal, 4 KV / 24 query heads"),
 }
 
 ORDER = ["tiny", "decode_27b", "mtp_verify", "long_agentic", "append_max_context"]
