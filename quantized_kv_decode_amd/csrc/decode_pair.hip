@@ -23,8 +23,9 @@
 //                   d = (D/16) n + (D/32) w + t, so lane n's V values again sit in one
 //                   scale group (a half group: D/64 code bytes per token).
 // Dequantisation work per token is that of the single-tile kernel; the accumulators
-// per wave are halved. A 256-thread workgroup holds two pairs that take alternate
-// blocks of one unit and merge at the end. Every wave runs the same number of block
+// per wave are halved. A workgroup holds kPairs pairs (4 at three or four row tiles: every
+// pair a CU keeps resident; 2 at two row tiles, three workgroups per CU) that take the
+// unit's blocks in turn and merge at the end. Every wave runs the same number of block
 // iterations (a pair with no block left runs a fully masked one on zero data), so the
 // workgroup barriers always match.
 #include "decode_common.h"
@@ -34,8 +35,6 @@ namespace {
 
 using namespace dev;
 
-constexpr int kPairs = 2;                       // wave pairs per workgroup
-constexpr uint32_t kPairStep = kBlockTokens * kPairs;   // tokens between a pair's blocks
 
 template <int D>
 struct PairRaw {
@@ -125,8 +124,11 @@ struct PairLds {
 };
 
 template <int D, int NT, bool DevLen>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_wgs_per_cu(NT))))
+__global__ __attribute__((amdgpu_flat_work_group_size(128 * decode_pairs_per_wg(NT), 128 * decode_pairs_per_wg(NT)),
+                          amdgpu_waves_per_eu(decode_wgs_per_cu(NT))))
 void decode_pair_kernel(DecodeParams p) {
+    constexpr int kPairs = decode_pairs_per_wg(NT);               // wave pairs per workgroup
+    constexpr uint32_t kPairStep = kBlockTokens * kPairs;         // tokens between a pair's blocks
     constexpr int KK = D / 32;
     constexpr int HT = D / 32;          // PV output tiles per wave (half of D/16)
     constexpr int EPL = D / 16;
@@ -356,23 +358,33 @@ void decode_pair_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * rt + 4 * g + i;
-            const float m0 = sm_m[0][row], m1 = sm_m[1][row];
-            const float M = fmaxf(m0, m1);
-            const float mp = pair ? m1 : m0;
+            float M = sm_m[0][row];
+#pragma unroll
+            for (int q = 1; q < kPairs; ++q) M = fmaxf(M, sm_m[q][row]);
+            const float mp = sm_m[pair][row];
             const float f = mp == -INFINITY ? 0.0f : exp2f(mp - M);
 #pragma unroll
             for (int t = 0; t < HT; ++t) acc[rt][t][i] *= f;
         }
     }
+    // pairs 1 .. kPairs - 1 hand their (rescaled) accumulators to pair 0 in turn, which
+    // adds them in that fixed order and writes the unit's partial
     float4_t(*mbuf)[HT][64] = reinterpret_cast<float4_t(*)[HT][64]>(big);   // [role][t][lane]
     float *ws_o = p.ws_o + ((int64_t)u * Rt + row0) * D;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-        if (pair == 1) {
+        for (int q = 1; q < kPairs; ++q) {
+            if (pair == q) {
 #pragma unroll
-            for (int t = 0; t < HT; ++t) mbuf[w][t][lane] = acc[rt][t];
+                for (int t = 0; t < HT; ++t) mbuf[w][t][lane] = acc[rt][t];
+            }
+            __syncthreads();
+            if (pair == 0) {
+#pragma unroll
+                for (int t = 0; t < HT; ++t) acc[rt][t] += mbuf[w][t][lane];
+            }
+            __syncthreads();
         }
-        __syncthreads();
         if (pair == 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -382,21 +394,22 @@ void decode_pair_kernel(DecodeParams p) {
 #pragma unroll
                     for (int t = 0; t < HT; t += 4)
                         *reinterpret_cast<float4_t *>(dst + t) =
-                            float4_t{acc[rt][t][i] + mbuf[w][t][lane][i], acc[rt][t + 1][i] + mbuf[w][t + 1][lane][i],
-                                     acc[rt][t + 2][i] + mbuf[w][t + 2][lane][i],
-                                     acc[rt][t + 3][i] + mbuf[w][t + 3][lane][i]};
+                            float4_t{acc[rt][t][i], acc[rt][t + 1][i], acc[rt][t + 2][i], acc[rt][t + 3][i]};
                 }
             }
         }
-        __syncthreads();
     }
     if (threadIdx.x < R) {
         const int row = threadIdx.x;
-        const float m0 = sm_m[0][row], m1 = sm_m[1][row];
-        const float M = fmaxf(m0, m1);
+        float M = sm_m[0][row];
+#pragma unroll
+        for (int q = 1; q < kPairs; ++q) M = fmaxf(M, sm_m[q][row]);
         float Ls = 0.f;
-        if (m0 != -INFINITY) Ls += exp2f(m0 - M) * sm_l[0][row];
-        if (m1 != -INFINITY) Ls += exp2f(m1 - M) * sm_l[1][row];
+#pragma unroll
+        for (int q = 0; q < kPairs; ++q) {
+            const float mq = sm_m[q][row];
+            if (mq != -INFINITY) Ls += exp2f(mq - M) * sm_l[q][row];
+        }
         p.ws_m[(int64_t)u * Rt + row0 + row] = M;
         p.ws_l[(int64_t)u * Rt + row0 + row] = Ls;
     }
@@ -405,9 +418,9 @@ void decode_pair_kernel(DecodeParams p) {
 template <int D, int NT>
 hipError_t launch_pair_t(const DecodeParams &p, hipStream_t s) {
     if (p.len_dev != nullptr)
-        hipLaunchKernelGGL((decode_pair_kernel<D, NT, true>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((decode_pair_kernel<D, NT, true>), dim3(p.units, p.grid_y), dim3(128 * decode_pairs_per_wg(NT)), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_pair_kernel<D, NT, false>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((decode_pair_kernel<D, NT, false>), dim3(p.units, p.grid_y), dim3(128 * decode_pairs_per_wg(NT)), 0, s, p);
     return hipGetLastError();
 }
 

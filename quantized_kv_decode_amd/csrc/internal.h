@@ -16,11 +16,17 @@ constexpr int kCUs = 256;            // compute units the split plan fills (MI35
 // Resident decode workgroups (256 threads) per CU that the partial kernel for NT row
 // tiles is built for: its waves per SIMD, set by its register budget.
 constexpr int decode_wgs_per_cu(int NT) { return NT == 2 ? 3 : 2; }
-// Units the split planner gives each CU. One row tile: one unit per CU, although two such
-// workgroups fit: half as many, twice as long units pay the per-unit start and merge half
-// as often (decode at 2 x 32k tokens: partial 21.6 -> 20.2 us; 600k: 123.1 -> 121.7 us).
-// Two to four row tiles: as many as stay resident (fewer was measured slower).
-constexpr int decode_units_per_cu(int NT) { return NT == 1 ? 1 : decode_wgs_per_cu(NT); }
+// Wave pairs per workgroup of the pair kernel (two to four row tiles). Three or four row
+// tiles: one workgroup holds every pair a CU keeps resident (8 waves); with several
+// workgroups per CU the later-dispatched ones ran slower and set the kernel's end, and one
+// workgroup halves the partials (mtp_verify step 58.9 -> 56.5 us). Two row tiles: two pairs,
+// three workgroups per CU (one 12-wave workgroup was slower: long_agentic 319 -> 334 us).
+constexpr int decode_pairs_per_wg(int NT) { return NT == 2 ? 2 : 4; }
+// Units the split planner gives each CU: one workgroup's worth, except two row tiles (three
+// workgroups). One row tile: although two such workgroups fit, half as many, twice as long
+// units pay the per-unit start and merge half as often (decode at 2 x 32k tokens: partial
+// 21.6 -> 20.2 us; 600k: 123.1 -> 121.7 us).
+constexpr int decode_units_per_cu(int NT) { return NT == 2 ? 3 : 1; }
 
 // Split-K plan: sequence b is cut into n_split[b] units of split_len[b] tokens
 // (a multiple of kBlockTokens) for each KV head; the last unit ends at the
