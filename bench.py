@@ -94,10 +94,26 @@ def cpu_baseline(w, budget_s: float = 12.0):
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 1000:
             break
+    # one thread, one step (a few seconds at these sizes): the per-core rate
+    t1 = time.perf_counter()
+    oracle.append(cache, kn, vn, g, w.seq_base, wp, [w.n_q] * w.batch, 1)
+    oracle.attention(cache, g, q, w.seq_base, w.seq_lens, w.n_q, w.sm_scale, nthreads=1)
+    el1 = time.perf_counter() - t1
     return {"value": round(w.kv_bytes * steps / el / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{steps} full decode step(s) of {w.name} (append n_q rows + fp64 attention for all "
                       f"{w.batch * w.n_q * w.num_q_heads} query rows over the whole cache), {el:.1f} s",
-            "ms_per_step": round(el / steps * 1e3, 3)}
+            "ms_per_step": round(el / steps * 1e3, 3),
+            "single_thread_ms_per_step": round(el1 * 1e3, 3), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main() -> int:
@@ -250,6 +266,34 @@ def main() -> int:
         wr = w.append_rows * w.num_kv_heads * (w.head_dim // 2 + w.head_dim // 16) * 2
         chunk_res = {"rows": w.append_rows, "us": round(ms_chunk * 1e3, 3), "bytes_read": rd, "bytes_written": wr,
                      "GBps": round((rd + wr) / (ms_chunk * 1e-3) / 1e9, 2)}
+    # spread of the step over repeated replays of the same graph (after the timed one)
+    reps = [time_graph(g_step) / K * 1e3 for _ in range(7)]
+    qs = sorted(reps)
+    spread = {"p10": round(qs[0], 3), "p50": round(qs[3], 3), "p90": round(qs[6], 3), "replays": 7}
+    # plain stream launches of the same K steps (no graph), between events
+    s0 = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(W):
+        step(i)
+    e0.record(s0)
+    for i in range(K):
+        step(i)
+    e1.record(s0)
+    e1.synchronize()
+    eager_us = e0.elapsed_time(e1) / K * 1e3
+    # with the cache allowed to stay in the 256 MB Infinity Cache (no rotation): labelled apart
+    warm_us = None
+    if R > 1:
+        sw = torch.cuda.Stream()
+        sw.wait_stream(torch.cuda.current_stream())
+        g_warm = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(sw):
+            with torch.cuda.graph(g_warm, stream=sw):
+                for i in range(K):
+                    k_decode_step(pools[0])
+        torch.cuda.current_stream().wait_stream(sw)
+        torch.cuda.synchronize()
+        warm_us = time_graph(g_warm) / K * 1e3
     # the same step with the lengths in device memory (nvfp4_decode_step_dev_len, bound = length),
     # which one captured graph can replay across steps; reported next to the main line
     lens_dev = torch.tensor(seq_lens, dtype=torch.int64, device=dev)
@@ -308,6 +352,9 @@ def main() -> int:
                      "kernel": "decode_partial", "algorithmic_bytes_per_launch": kv},
     }
     res["device_lengths_step_us"] = round(ms_dl * 1e3, 3) if dev_len else None
+    res["step_us_spread"] = spread
+    res["stream_launch_step_us"] = round(eager_us, 3)
+    res["warm_infinity_cache_step_us"] = round(warm_us, 3) if warm_us is not None else None
     # attention arithmetic of the step (QK^T and PV over the visible keys, 2 flops per
     # multiply-add), against MI355X's dense fp16 matrix peak: the bound for long query chunks
     res["attention_tflops"] = round(w.flops / (ms_step * 1e-3) / 1e12, 2)
