@@ -13,9 +13,10 @@
 // of a pair share each block:
 //   S^T = K . Q^T   wave w (0/1) takes the 16-token tile w of the block, all rows,
 //                   full head_dim (same fragment layout as the single-tile kernel);
-//   softmax         each wave reduces its 16 tokens per row; the pair agrees on the
-//                   running reference m through LDS (barrier 1), then each wave
-//                   writes its fp16 probabilities to LDS (barrier 2);
+//   softmax         each wave writes fp16 probabilities of its 16 tokens to LDS against
+//                   the pair's running reference m; the row maxima are reduced and
+//                   exchanged only in a block where some score passes m by the lazy
+//                   margin (then the pair moves m, rescales and rewrites);
 //   O += P . V      each wave reads the whole 32-token P (its own and its partner's,
 //                   lane for lane: lane (g, n) of wave w holds exactly the k-slots
 //                   4 w .. 4 w + 3 of lane (g, n)'s A operand) and multiplies it into
@@ -26,7 +27,8 @@
 // per wave are halved. A workgroup holds kPairs pairs (4 at three or four row tiles: every
 // pair a CU keeps resident; 2 at two row tiles, three workgroups per CU) that take the
 // unit's blocks in turn and merge at the end. Every wave runs the same number of block
-// iterations (a pair with no block left runs a fully masked one on zero data), so the
+// iterations (a pair with no block left runs a fully masked one on zero data), and the
+// choice of a reference update is read by every wave from the same LDS bytes, so the
 // workgroup barriers always match.
 #include "decode_common.h"
 
@@ -35,6 +37,11 @@ namespace {
 
 using namespace dev;
 
+
+// The reference m of a row moves only when a score passes m + kPairLazy (base 2), so fp16
+// probabilities stay below 2^15 (finite: the fp16 maximum is about 2^16) and a unit's reference
+// settles after its first blocks: every later move costs the whole workgroup an exchange.
+constexpr float kPairLazy = 15.0f;
 
 template <int D>
 struct PairRaw {
@@ -135,7 +142,8 @@ void decode_pair_kernel(DecodeParams p) {
     using LD = PairLds<D, NT>;
     __shared__ __attribute__((aligned(16))) uint8_t big[LD::BIG];
     __shared__ __attribute__((aligned(16))) u32x4_t pbuf[kPairs][2][NT][64];   // [pair][parity]: fp16 P per lane
-    __shared__ float xmax[kPairs][2][2][NT * 16];                         // [pair][parity][half]
+    __shared__ float xmax[kPairs][2][NT * 16];                            // [pair][half]
+    __shared__ __attribute__((aligned(8))) uint8_t mflag[2][8];           // [parity][wave]
     __shared__ float sm_c[kMaxRows];
     __shared__ float sm_m[kPairs][kMaxRows];
     __shared__ float sm_l[kPairs][kMaxRows];
@@ -184,6 +192,7 @@ void decode_pair_kernel(DecodeParams p) {
         pair_load_v<D>(r, vc, vs, o0);
     }
     if (wave < NT) q_store<D>(p, rw, b, kh, wave, lane, qw, qlds, sm_c);
+    if (threadIdx.x < 16) (&mflag[0][0])[threadIdx.x] = 0;   // bytes of absent waves stay 0
     __syncthreads();
     float cexp[NT];
     int qi[NT];
@@ -197,30 +206,53 @@ void decode_pair_kernel(DecodeParams p) {
     float4_t acc[NT][HT];    // rows 16 rt + 4 g + i, d = EPL n + HT w + t
     float4_t lsum[NT];       // wave 0 of the pair: P . 1 over the same rows
     float m[NT];             // pair-wide reference of row 16 rt + n (base 2)
+    float thr[NT];           // m + kPairLazy: a score above it moves the reference
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
         m[rt] = -INFINITY;
+        thr[rt] = -INFINITY;
         lsum[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < HT; ++t) acc[rt][t] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
     const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
 
-    // The pair's j-th block is block pair + 2 j of the unit. One loop trip finishes block j
-    // and starts block j + 1, so the softmax chain and the barrier waits of block j overlap
-    // the dequantisation and MFMAs of block j + 1:
-    //   barrier A  -> partner's row maxima of block j -> reference m, P(j) to LDS;
-    //                 V(j) interleave, V(j + 1) loads; S^T(j + 1), K(j + 2) loads,
-    //                 scores and row maxima of block j + 1 to LDS (other parity)
-    //   barrier B  -> P(j) of both halves -> O += P(j) . V(j)
+    // The pair's j-th block is block pair + kPairs j of the unit. Probabilities are written
+    // speculatively: right after its scores, each wave turns block j's scores into fp16
+    // P = 2^(x - m) with the reference m it holds, stores them (LDS, parity j & 1) and
+    // raises its byte in mflag[j & 1] if any score lies above m + kPairLazy. After the
+    // barrier every wave reads all the bytes, so the decision is the workgroup's:
+    //   none raised (the common case once the first block has set m): P(j) in LDS is final
+    //     and O += P(j) . V(j) follows at once -- no row maximum is reduced or exchanged;
+    //   some raised: every pair reduces its rows' maxima of block j, exchanges them through
+    //     LDS (barrier), moves m where it is exceeded by more than kPairLazy, rescales O and
+    //     l, rewrites P(j) (barrier) -- exactly the update a per-block exchange would make,
+    //     so the result does not depend on which path ran.
+    // One loop trip: barrier -> [update] -> O += P(j) . V(j); V(j + 1) interleave, V(j + 2)
+    // loads; S^T(j + 1), K(j + 2) loads, P(j + 1) and its flag.
     // lim: offset limit of the block relative to L - n_q (32-bit: tokens < 2^31).
     const int lim0 = (int)(un.L - p.n_q - un.t0) - kBlockTokens * pair;
     const int iters = max((nblk + kPairs - 1) / kPairs, 1);   // an empty unit runs one masked trip
-    float x[NT][4], mloc[NT];
+    float x[NT][4];
 
-    // S^T of the pair's block j from the K words in r, the K loads of block j + 1, and
-    // the block's masked scores and row maxima (published in xmax[j & 1]). A block past
-    // the pair's last one masks everything (its words are zeros).
+    // fp16 probabilities of this wave's 16 tokens of block j, relative to m, into LDS
+    auto write_p = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const float mu = m[rt] == -INFINITY ? 0.0f : m[rt];
+            const half2_t p01 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][0] - mu),
+                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][1] - mu)};
+            const half2_t p23 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][2] - mu),
+                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][3] - mu)};
+            uint32_t *dst = reinterpret_cast<uint32_t *>(&pbuf[pair][j & 1][rt][lane]) + 2 * w;
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{as_u32(p01), as_u32(p23)};
+        }
+    };
+
+    // S^T of the pair's block j from the K words in r, the K loads of block j + 1, the
+    // block's masked scores, its speculative probabilities and this wave's flag. A block
+    // past the pair's last one masks everything (its words are zeros).
     auto start_block = [&](int j) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");     // Q fragments are re-read from LDS every block
         float4_t s[NT];
@@ -246,18 +278,59 @@ void decode_pair_kernel(DecodeParams p) {
                 for (int i = 0; i < 4; ++i)
                     if (16 * w + 4 * g + i > lim + qi[rt]) x[rt][i] = -INFINITY;
         }
+        bool above = false;
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) above |= x[rt][i] > thr[rt];
+        write_p(j);
+        const uint8_t flag = __builtin_amdgcn_ballot_w64(above) != 0 ? 1 : 0;   // all lanes vote
+        if (lane == 0) mflag[j & 1][wave] = flag;
+    };
+
+    // The reference update for block j (every wave of the workgroup, see above).
+    auto update = [&](int j) __attribute__((always_inline)) {
+        float mloc[NT];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             mloc[rt] = wave_max_g(fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3])));
-            if (g == 0) xmax[pair][j & 1][w][16 * rt + n] = mloc[rt];
+            if (g == 0) xmax[pair][w][16 * rt + n] = mloc[rt];
         }
+        __syncthreads();
+        bool need_any = false;
+        float alpha[NT];
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+            const float mb = fmaxf(mloc[rt], xmax[pair][1 - w][16 * rt + n]);
+            const bool need = mb > m[rt] + kPairLazy;   // both waves of the pair see the same values
+            const float mnew = need ? mb : m[rt];
+            alpha[rt] = need ? exp2f(m[rt] - mnew) : 1.0f;   // m = -inf -> 0
+            m[rt] = mnew;
+            thr[rt] = mnew + kPairLazy;
+            need_any |= need;
+        }
+        if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha[rt], 4 * g + i);   // accumulator row 4 g + i
+                    lsum[rt][i] *= ai;
+#pragma unroll
+                    for (int t = 0; t < HT; ++t) acc[rt][t][i] *= ai;
+                }
+            }
+        }
+        write_p(j);
+        __syncthreads();
     };
 
     // O += P(j) . V(j) over this wave's half of head_dim, P(j) of both waves from LDS.
-    auto pv_block = [&](int j, const PairVPrep &vp) __attribute__((always_inline)) {
-        half8_t pa[NT];
+    auto read_p = [&](int j, half8_t (&pa)[NT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) pa[rt] = __builtin_bit_cast(half8_t, pbuf[pair][j & 1][rt][lane]);
+    };
+    auto pv_block = [&](const half8_t (&pa)[NT], const PairVPrep &vp) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < HT; ++t) {
             uint32_t bw[4];
@@ -285,63 +358,29 @@ void decode_pair_kernel(DecodeParams p) {
         }
     };
 
-    // One loop trip per block j of the pair, with ONE workgroup barrier: it publishes the
-    // row maxima of block j and the probabilities of block j - 1 of both waves. After it,
-    // each wave fixes the reference m for block j, writes P(j) (LDS, parity j & 1), multiplies
-    // P(j - 1) into O, interleaves V(j), issues the loads of block j + 1 and computes S^T of
-    // block j + 1 -- one straight stretch of independent matrix and vector work. The rare
-    // rescale of O by exp2(m_old - m_new) comes last: O then holds blocks up to j - 1, all
-    // relative to m_old, and P(j) (relative to m_new) is multiplied in on the next trip.
-    PairVPrep vprev;
-    auto trip = [&](int j, bool do_pv, bool do_next) __attribute__((always_inline)) {
-        __syncthreads();
-        bool need_any = false;
-        float alpha[NT];
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            const float mb = fmaxf(mloc[rt], xmax[pair][j & 1][1 - w][16 * rt + n]);
-            const bool need = mb > m[rt] + kLazyMax;   // both waves of the pair see the same values
-            const float mnew = need ? mb : m[rt];
-            alpha[rt] = need ? exp2f(m[rt] - mnew) : 1.0f;   // m = -inf -> 0
-            m[rt] = mnew;
-            need_any |= need;
+    PairVPrep vprep;
+    auto trip = [&](int j, bool do_next) __attribute__((always_inline)) {
+        __syncthreads();                   // P(j) and the flags of every wave
+        const uint32_t f0 = __builtin_amdgcn_readfirstlane(reinterpret_cast<const volatile uint32_t *>(mflag[j & 1])[0]);
+        const uint32_t f1 = __builtin_amdgcn_readfirstlane(reinterpret_cast<const volatile uint32_t *>(mflag[j & 1])[1]);
+        half8_t pa[NT];
+        read_p(j, pa);                     // final unless the update below rewrites P(j)
+        if ((f0 | f1) != 0) {
+            update(j);
+            read_p(j, pa);
         }
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-            const float mu = m[rt] == -INFINITY ? 0.0f : m[rt];
-            const half2_t p01 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][0] - mu),
-                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][1] - mu)};
-            const half2_t p23 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][2] - mu),
-                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][3] - mu)};
-            uint32_t *dst = reinterpret_cast<uint32_t *>(&pbuf[pair][j & 1][rt][lane]) + 2 * w;
-            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{as_u32(p01), as_u32(p23)};
-        }
-        if (do_pv) pv_block(j - 1, vprev);
-        pair_v_prep<D>(vprev, r);
+        pv_block(pa, vprep);
+        pair_v_prep<D>(vprep, r);
         __builtin_amdgcn_sched_barrier(0);
-        pair_load_v<D>(r, vc, vs, offs_for(pair + kPairs * (j + 1)));
+        pair_load_v<D>(r, vc, vs, offs_for(pair + kPairs * (j + 2)));
         if (do_next) start_block(j + 1);
-        if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
-#pragma unroll
-            for (int rt = 0; rt < NT; ++rt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha[rt], 4 * g + i);   // accumulator row 4 g + i
-                    lsum[rt][i] *= ai;
-#pragma unroll
-                    for (int t = 0; t < HT; ++t) acc[rt][t][i] *= ai;
-                }
-            }
-        }
     };
 
     start_block(0);
-    trip(0, false, iters > 1);
-    for (int j = 1; j < iters - 1; ++j) trip(j, true, true);
-    if (iters > 1) trip(iters - 1, true, false);
-    __syncthreads();                                       // P of the last block
-    pv_block(iters - 1, vprev);
+    pair_v_prep<D>(vprep, r);
+    pair_load_v<D>(r, vc, vs, offs_for(pair + kPairs));
+    for (int j = 0; j < iters - 1; ++j) trip(j, true);
+    trip(iters - 1, false);
 
     // ---- merge the two pairs and write the unit's partial
 #pragma unroll
