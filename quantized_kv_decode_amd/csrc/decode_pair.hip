@@ -202,6 +202,13 @@ void decode_pair_kernel(DecodeParams p) {
         cexp[rt] = sm_c[row];
         qi[rt] = row < R ? (row0 + row) / G : p.n_q;  // padded rows see every key (their q is 0)
     }
+    // At three row tiles the first tile's Q fragments stay in registers (KK x 4 VGPRs, room
+    // left at two waves per SIMD): a third less LDS read traffic in the score stage, where the
+    // eight waves of the CU otherwise queue on LDS together.
+    constexpr int kQReg = NT == 3 ? 1 : 0;
+    half8_t qreg[kQReg ? KK : 1];
+#pragma unroll
+    for (int kk = 0; kk < (kQReg ? KK : 0); ++kk) qreg[kk] = qlds[kk * 64 + lane];
 
     float4_t acc[NT][HT];    // rows 16 rt + 4 g + i, d = EPL n + HT w + t
     float4_t lsum[NT];       // wave 0 of the pair: P . 1 over the same rows
@@ -263,7 +270,8 @@ void decode_pair_kernel(DecodeParams p) {
             const half8_t a = pair_dequant_k<D>(r, kk);
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt)
-                s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qlds[(rt * KK + kk) * 64 + lane], s[rt], 0, 0, 0);
+                s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, rt < kQReg ? qreg[kk] : qlds[(rt * KK + kk) * 64 + lane],
+                                                               s[rt], 0, 0, 0);
         }
         pair_load_k<D>(r, kc, ks, offs_for(pair + kPairs * (j + 1)));
         const int lim = pair + kPairs * j < nblk ? lim0 - (int)kPairStep * j : -(1 << 30);
