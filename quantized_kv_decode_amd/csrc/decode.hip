@@ -9,8 +9,10 @@
 // Work decomposition. A unit is (sequence b, KV head kh, token range); one
 // 256-thread workgroup runs one unit, its four waves taking alternate 32-token
 // blocks. Every query row that reads KV head kh -- GQA group G times n_q query
-// tokens, R <= 64 rows, padded to NT tiles of 16 -- shares each KV block, so a
-// block is loaded and dequantised once for all of them.
+// tokens, padded to NT tiles of 16 -- shares each KV block, so a block is loaded
+// and dequantised once for all of them. This kernel serves one or two row tiles
+// (up to 32 rows: at two, 256 VGPRs, two waves per SIMD); three or four go to the
+// wave-pair kernel, whose waves split each block.
 //
 // Per 32-token block and wave (MFMA v_mfma_f32_16x16x32_f16, lane l = 16 g + n):
 //   S^T = K . Q^T   A = K (16 tokens x 32 d), B = Q^T (32 d x 16 rows), two token
@@ -284,7 +286,7 @@ struct Lds {
 };
 
 template <int D, int NT, bool DevLen>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_wgs_per_cu(NT))))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_waves_per_simd(NT))))
 void decode_partial_kernel(DecodeParams p) {
     constexpr int KK = D / 32;
     constexpr int EPL = D / 16;
@@ -570,9 +572,9 @@ hipError_t launch_partial_t(const DecodeParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream_t s) {
-    if (NT != 1) return launch_decode_pair(p, D, NT, s);
-    if (D == 256) return launch_partial_t<256, 1>(p, s);
-    if (D == 128) return launch_partial_t<128, 1>(p, s);
+    if (NT > 2) return launch_decode_pair(p, D, NT, s);
+    if (D == 256) return NT == 1 ? launch_partial_t<256, 1>(p, s) : launch_partial_t<256, 2>(p, s);
+    if (D == 128) return NT == 1 ? launch_partial_t<128, 1>(p, s) : launch_partial_t<128, 2>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -1,4 +1,4 @@
-// Split-K decode partial for two to four row tiles (17..64 query rows per KV head):
+// Split-K decode partial for three or four row tiles (33..64 query rows per KV head):
 // the wave-pair kernel (gfx950).
 //
 // It computes what the single-tile kernel computes (gzenz/ninfer page, "Context and
@@ -24,9 +24,8 @@
 //                   d = (D/16) n + (D/32) w + t, so lane n's V values again sit in one
 //                   scale group (a half group: D/64 code bytes per token).
 // Dequantisation work per token is that of the single-tile kernel; the accumulators
-// per wave are halved. A workgroup holds kPairs pairs (4 at three or four row tiles: every
-// pair a CU keeps resident; 2 at two row tiles, three workgroups per CU) that take the
-// unit's blocks in turn and merge at the end. Every wave runs the same number of block
+// per wave are halved. A workgroup holds kPairs = 4 pairs (every pair a CU keeps resident)
+// that take the unit's blocks in turn and merge at the end. Every wave runs the same number of block
 // iterations (a pair with no block left runs a fully masked one on zero data), and the
 // choice of a reference update is read by every wave from the same LDS bytes, so the
 // workgroup barriers always match.
@@ -132,7 +131,7 @@ struct PairLds {
 
 template <int D, int NT, bool DevLen>
 __global__ __attribute__((amdgpu_flat_work_group_size(128 * decode_pairs_per_wg(NT), 128 * decode_pairs_per_wg(NT)),
-                          amdgpu_waves_per_eu(decode_wgs_per_cu(NT))))
+                          amdgpu_waves_per_eu(decode_waves_per_simd(NT))))
 void decode_pair_kernel(DecodeParams p) {
     constexpr int kPairs = decode_pairs_per_wg(NT);               // wave pairs per workgroup
     constexpr uint32_t kPairStep = kBlockTokens * kPairs;         // tokens between a pair's blocks
@@ -476,13 +475,11 @@ hipError_t launch_pair_t(const DecodeParams &p, hipStream_t s) {
 hipError_t launch_decode_pair(const DecodeParams &p, int D, int NT, hipStream_t s) {
     if (D == 256) {
         switch (NT) {
-            case 2: return launch_pair_t<256, 2>(p, s);
             case 3: return launch_pair_t<256, 3>(p, s);
             case 4: return launch_pair_t<256, 4>(p, s);
         }
     } else if (D == 128) {
         switch (NT) {
-            case 2: return launch_pair_t<128, 2>(p, s);
             case 3: return launch_pair_t<128, 3>(p, s);
             case 4: return launch_pair_t<128, 4>(p, s);
         }

@@ -13,20 +13,22 @@ constexpr int kBlockTokens = 32;     // tokens per KV block: one PV MFMA K-step 
 constexpr int kWaves = 4;            // waves per decode workgroup (256 threads)
 constexpr int kCUs = 256;            // compute units the split plan fills (MI355X)
 
-// Resident decode workgroups (256 threads) per CU that the partial kernel for NT row
-// tiles is built for: its waves per SIMD, set by its register budget.
-constexpr int decode_wgs_per_cu(int NT) { return NT == 2 ? 3 : 2; }
-// Wave pairs per workgroup of the pair kernel (two to four row tiles). Three or four row
-// tiles: one workgroup holds every pair a CU keeps resident (8 waves); with several
-// workgroups per CU the later-dispatched ones ran slower and set the kernel's end, and one
-// workgroup halves the partials (mtp_verify step 58.9 -> 56.5 us). Two row tiles: two pairs,
-// three workgroups per CU (one 12-wave workgroup was slower: long_agentic 319 -> 334 us).
-constexpr int decode_pairs_per_wg(int NT) { return NT == 2 ? 2 : 4; }
-// Units the split planner gives each CU: one workgroup's worth, except two row tiles (three
-// workgroups). One row tile: although two such workgroups fit, half as many, twice as long
-// units pay the per-unit start and merge half as often (decode at 2 x 32k tokens: partial
-// 21.6 -> 20.2 us; 600k: 123.1 -> 121.7 us).
-constexpr int decode_units_per_cu(int NT) { return NT == 2 ? 3 : 1; }
+// Waves per SIMD that the partial kernel for NT row tiles is built for, set by its register
+// budget: two everywhere (one or two row tiles: the single-wave-per-block kernel, up to 256
+// VGPRs; three or four: the pair kernel, one 8-wave workgroup per CU).
+constexpr int decode_waves_per_simd(int /*NT*/) { return 2; }
+// Wave pairs per workgroup of the pair kernel (three or four row tiles): one workgroup holds
+// every pair a CU keeps resident (8 waves); with several workgroups per CU the
+// later-dispatched ones ran slower and set the kernel's end, and one workgroup halves the
+// partials (mtp_verify step 58.9 -> 56.5 us).
+constexpr int decode_pairs_per_wg(int /*NT*/) { return 4; }
+// Units the split planner gives each CU. One row tile: one, although two such workgroups
+// fit -- half as many, twice as long units pay the per-unit start and merge half as often
+// (decode at 2 x 32k tokens: partial 21.6 -> 20.2 us; 600k: 123.1 -> 121.7 us). Two row
+// tiles: two, one per resident workgroup (three sessions of 330k-470k tokens, 24 rows:
+// partial 268.8 us with one unit per CU, 261.4 with two, 271.8 with four). Three or four:
+// one 8-wave workgroup.
+constexpr int decode_units_per_cu(int NT) { return NT == 2 ? 2 : 1; }
 
 // Split-K plan: sequence b is cut into n_split[b] units of split_len[b] tokens
 // (a multiple of kBlockTokens) for each KV head; the last unit ends at the
