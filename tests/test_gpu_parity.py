@@ -101,6 +101,8 @@ DECODE_SHAPES = [
     dict(seq_lens=(2050,), num_kv_heads=2, num_q_heads=2, head_dim=128, n_q=5),                            # G = 1
     dict(seq_lens=(333, 100), num_kv_heads=1, num_q_heads=16, head_dim=256, n_q=4),                       # 64 rows
     dict(seq_lens=(257,), num_kv_heads=1, num_q_heads=8, head_dim=128, n_q=6),                            # 48 rows
+    dict(seq_lens=(1500, 45), num_kv_heads=2, num_q_heads=8, head_dim=128, n_q=5),                        # 20 rows, D 128
+    dict(seq_lens=(1234,), num_kv_heads=2, num_q_heads=16, head_dim=256, n_q=4, outlier_frac=0.02),      # 32 rows
     # wide draft windows: two row chunks over one split plan
     dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=16),   # 96 rows: 48 + 48
     dict(seq_lens=(900, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=12, v_dist="laplace"),  # 72: 48 + 24
@@ -202,6 +204,7 @@ DEV_LEN_CASES = [
     (dict(seq_lens=(512,), num_kv_heads=1, num_q_heads=4, head_dim=128, n_q=1), 0),          # bound = length
     (dict(seq_lens=(1000, 77, 3), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=1), 700),
     (dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=4), 3000),   # 24 rows
+    (dict(seq_lens=(1500, 45), num_kv_heads=2, num_q_heads=8, head_dim=128, n_q=5), 2500),    # 20 rows, D 128
     (dict(seq_lens=(963,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6, outlier_frac=0.02), 5000),
     (dict(seq_lens=(6, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6), 100000),     # nearly all units empty
     (dict(seq_lens=(9, 20), num_kv_heads=1, num_q_heads=4, head_dim=256, n_q=1), 60000),      # one row tile, same
