@@ -20,10 +20,10 @@
 //                   D/8 contiguous code bytes + D/64 scale bytes. The contraction
 //                   index d is permuted identically in Q, so no transpose is needed.
 //                   Result lane (g, n): tokens 16 mt + 4 g + i, row 16 rt + n.
-//   softmax         fp32, base 2, per row (lane column n); cross-lane max over the
-//                   four lane groups only; the running reference m is raised
-//                   lazily (only when a score exceeds it by more than 2^8), so the
-//                   accumulator rescale is rare.
+//   softmax         fp32, base 2, per row (lane column n); the running reference m
+//                   is raised lazily (only when a score exceeds it by more than 8,
+//                   base 2), tested lane by lane, so the cross-lane row maximum and
+//                   the accumulator rescale are both rare.
 //   O += P . V      A = P (16 rows x 32 tokens, straight from the S^T layout),
 //                   B = V (32 tokens x 16 d). The d index of output column n of
 //                   tile dt is EPL n + dt (EPL = D/16), so lane n's B values for
@@ -114,6 +114,8 @@ struct State {
     float4_t acc[NT][EPL];   // O rows 16 rt + 4 g + i, d = EPL n + dt
     float4_t lsum[NT];       // row sums of the fp16 P actually multiplied into O (P . 1), same rows
     float m[NT];             // running reference of row 16 rt + n (base 2)
+    float nmu[NT];           // -m, or 0 while m = -inf (the exponent offset of P)
+    float thr[NT];           // m + kLazyMax: a block maximum above it moves m
 };
 
 template <int D>
@@ -182,14 +184,23 @@ __device__ inline void v_prep(VPrep<D> &vp, const Raw<D> &r) {
 // Scores -> probabilities for one block. lim = L - n_q - tb: key at offset o of the
 // block is visible to query token i iff o <= lim + i (bottom-right causal; offsets
 // past the sequence end are never visible). Blocks with lim >= 31 need no mask; the
-// mask is applied in place, so both cases leave the scores in the same registers.
+// mask is applied in place to the raw MFMA scores (masked: -inf).
+//
+// The scaled score of key j in row r is x = c_r s_j with c_r > 0 (q_store keeps it
+// positive), so max_j x = c_r max_j s_j (rounding is monotone). The reference m of a row
+// moves only when its block maximum passes m + kLazyMax; that is tested lane by lane
+// first (each lane holds 8 of the row's 32 keys), and only when some lane passes does
+// the wave reduce the row maxima across lanes and move m -- the same decisions, and the
+// same m, as a reduction in every block. P = 2^(c s - m) takes one fma per score.
 template <int D, int NT>
-__device__ inline void scores_block(float (&x)[NT][8], float (&mrow)[NT], const float4_t (&s)[2][NT],
-                                    const float (&cexp)[NT], const int (&qi)[NT], int lim, int g) {
+__device__ inline void softmax_block(State<D, NT> &st, const float4_t (&s)[2][NT], half8_t (&pa)[NT],
+                                     const float (&cexp)[NT], const int (&qi)[NT], int lim, int g) {
+    constexpr int EPL = D / 16;
+    float x[NT][8];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[rt][j] = s[j >> 2][rt][j & 3] * cexp[rt];
+        for (int j = 0; j < 8; ++j) x[rt][j] = s[j >> 2][rt][j & 3];
     if (lim < kBlockTokens - 1) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
@@ -199,31 +210,23 @@ __device__ inline void scores_block(float (&x)[NT][8], float (&mrow)[NT], const 
                 if (o > lim + qi[rt]) x[rt][j] = -INFINITY;
             }
     }
+    float lmax[NT];
+    bool above = false;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-        float mloc = x[rt][0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, x[rt][j]);
-        mrow[rt] = wave_max_g(mloc);
+        lmax[rt] = max8(x[rt]) * cexp[rt];
+        above |= lmax[rt] > st.thr[rt];
     }
-}
-
-template <int D, int NT>
-__device__ inline void softmax_block(State<D, NT> &st, const float4_t (&s)[2][NT], half8_t (&pa)[NT],
-                                     const float (&cexp)[NT], const int (&qi)[NT], int lim, int g) {
-    constexpr int EPL = D / 16;
-    float x[NT][8], mrow[NT];
-    scores_block<D, NT>(x, mrow, s, cexp, qi, lim, g);
-    bool need_any = false;
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) need_any |= mrow[rt] > st.m[rt] + kLazyMax;
-    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {   // rare after the first block
+    if (__builtin_amdgcn_ballot_w64(above) != 0) {   // rare after the first block
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
-            const bool need = mrow[rt] > st.m[rt] + kLazyMax;
-            const float mnew = need ? mrow[rt] : st.m[rt];
+            const float mrow = wave_max_g(lmax[rt]);
+            const bool need = mrow > st.thr[rt];
+            const float mnew = need ? mrow : st.m[rt];
             const float alpha = need ? exp2f(st.m[rt] - mnew) : 1.0f;   // m = -inf -> 0
             st.m[rt] = mnew;
+            st.nmu[rt] = mnew == -INFINITY ? 0.0f : -mnew;
+            st.thr[rt] = mnew + kLazyMax;
             // accumulator rows 4 g + i live in lane column n' = 4 g + i
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -236,10 +239,9 @@ __device__ inline void softmax_block(State<D, NT> &st, const float4_t (&s)[2][NT
     }
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-        const float mu = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(x[rt][j] - mu);   // v_exp_f32
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(x[rt][j], cexp[rt], st.nmu[rt]));   // v_exp_f32
         pa[rt] = half8_t{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
                          (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
     }
@@ -356,6 +358,8 @@ void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
         st.m[rt] = -INFINITY;
+        st.nmu[rt] = 0.0f;
+        st.thr[rt] = -INFINITY;
         st.lsum[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < EPL; ++dt) st.acc[rt][dt] = float4_t{0.f, 0.f, 0.f, 0.f};

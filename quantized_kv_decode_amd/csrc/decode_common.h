@@ -19,6 +19,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyMax = 8.0f;      // raise the softmax reference only past m + 8 (base 2)
+// Smallest score factor (see q_store). MFMA scores are below 2^27 in magnitude (|q| < 2^15
+// per element after scaling, |k_hat'| <= 6 * 448 * 2^-8 = 10.5, 256 terms), so a score times
+// this is below 2^-72.
+constexpr float kMinScoreScale = 1e-30f;
 
 __device__ inline half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
 __device__ inline uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -45,6 +49,18 @@ __device__ inline float wave_max_g(float x) {
     const uint32_t yb = __builtin_bit_cast(uint32_t, y);
     const auto c = __builtin_amdgcn_permlane32_swap(yb, yb, false, false);
     return fmaxf(__builtin_bit_cast(float, (uint32_t)c[0]), __builtin_bit_cast(float, (uint32_t)c[1]));
+}
+
+// Maximum of 8 scores in four VALU instructions. Written out because fmaxf on values the
+// compiler cannot prove quiet (MFMA results, masked -inf) gets a quieting v_max x, x per
+// operand first; scores are never NaN.
+__device__ inline float max8(const float (&x)[8]) {
+    float a, b, c, r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(a) : "v"(x[0]), "v"(x[1]), "v"(x[2]));
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(b) : "v"(x[3]), "v"(x[4]), "v"(x[5]));
+    asm("v_max_f32 %0, %1, %2" : "=v"(c) : "v"(x[6]), "v"(x[7]));
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -182,7 +198,11 @@ __device__ inline void append_step_rows(const DecodeParams &p, int b, int kh, in
 // Each row is scaled by an exact power of two that brings its maximum magnitude to
 // [2^14, 2^15) before the fp16 conversion; sm_c[row] receives the factor that turns an
 // MFMA score back into sm_scale * q . k_hat * log2(e) (including the 2^8 of the
-// dequantised K and g_K). Rows past R get zero fragments and factor 0.
+// dequantised K and g_K). The factor is kept positive: the sign of sm_scale goes into
+// the fragments (an exact negation), and a zero factor (g_K = 0, sm_scale = 0, rows past
+// R, whose fragments are zero) becomes kMinScoreScale, which leaves every finite score
+// within 2^-72 of 0 and keeps a masked score (-inf) at -inf. Rows past R get zero
+// fragments.
 template <int D>
 __device__ inline void q_load(const DecodeParams &p, const Rows &rw, int b, int kh, int rt, int lane,
                               uint32_t (&w)[D / 8]) {
@@ -219,7 +239,7 @@ __device__ inline void q_store(const DecodeParams &p, const Rows &rw, int b, int
     am = max(am, (uint32_t)__shfl_xor((int)am, 32));
     const int e = (int)((am >> 7) & 0xFF) - 127;
     const int shift = am ? min(max(14 - e, -100), 100) : 0;
-    const float qs = ldexpf(1.0f, shift);
+    const float qs = p.sm_scale < 0.0f ? -ldexpf(1.0f, shift) : ldexpf(1.0f, shift);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         u32x4_t hv;
@@ -234,7 +254,8 @@ __device__ inline void q_store(const DecodeParams &p, const Rows &rw, int b, int
     }
     if (g == 0) {
         const float gk = p.gscale[(b * p.Hkv + kh) * 2 + 0];
-        sm_c[row] = row < rw.Rc ? p.sm_scale * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
+        const float c = row < rw.Rc ? fabsf(p.sm_scale) * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
+        sm_c[row] = fmaxf(c, kMinScoreScale);
     }
 }
 

@@ -344,6 +344,25 @@ def test_extreme_scores_and_constant_v(qk):
     assert torch.allclose(o[:, :, 4:], torch.full_like(o[:, :, 4:], -0.75), rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("scale", [-0.0625, 0.0])
+def test_nonpositive_softmax_scale(qk, scale):
+    """A negative softmax scale (the kernels put its sign into the query fragments and keep
+    a positive score factor) and a zero one (uniform weights), on one, two and three row
+    tiles."""
+    for shape in (dict(seq_lens=(300, 45), num_kv_heads=2, num_q_heads=6, head_dim=256, n_q=1),
+                  dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=4),
+                  dict(seq_lens=(963,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6)):
+        w = workloads.small(**shape)
+        say("sm_scale", scale, shape)
+        ref = OracleRun(w)
+        pool, g, _ = gpu_run(w, ref.k, ref.v, ref.q)
+        out = qk.decode_attn(pool, g, ref.q.cuda(), w.seq_base, list(w.seq_lens), scale)
+        exp = oracle.attention(ref.cache, ref.g, workloads.as_u16(ref.q), w.seq_base, w.seq_lens, w.n_q, scale)
+        err, tol = max_err(out.float().cpu().numpy(), exp), TOL_REL * ref.vmax()
+        say(f"  max err {err:.3e}  tol {tol:.3e}")
+        assert err <= tol
+
+
 def test_sequence_at_pool_end_and_zero_kv(qk):
     """A sequence ending exactly at the pool's last slot with a ragged tail (reads past
     the end stay in bounds), all-zero K (uniform weights) and all-zero V."""
