@@ -124,10 +124,10 @@ size_t nvfp4_decode_attn_workspace_bytes(const nvfp4_kv_cache *cache, int32_t nu
  *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
  *   out = softmax(sm_scale * q . k_hat) . v_hat, computed with fp32 accumulation.
  *   Up to 64 query rows per KV head ((num_q_heads/num_kv_heads) * n_q) are served by one
- *   pass over the cache; 65..128 rows (wide draft windows, e.g. n_q = 16 at a GQA group
- *   of 6) by two passes over balanced halves of the rows, so the KV bytes are read twice;
- *   129..8192 rows (a prefill chunk attending to the cache and, causally, to itself) by
- *   row chunks of at most 64 side by side, each skipping the keys its rows cannot see.
+ *   pass over the cache; 65..8192 rows (wide draft windows, e.g. n_q = 16 at a GQA group
+ *   of 6, and prefill chunks attending to the cache and, causally, to themselves) by
+ *   32-row chunks side by side in one launch, each chunk reading the KV blocks its rows
+ *   can see (chunks of one unit run at the same time, so most repeated reads hit cache).
  * Errors: EINVAL (pointers, out_dtype, n_q < 1, non-finite sm_scale),
  *         EUNSUPPORTED (head_dim, num_q_heads % num_kv_heads != 0, num_seqs > 8,
  *         (num_q_heads/num_kv_heads) * n_q > 8192), ERANGE (seq_len < n_q, slots past

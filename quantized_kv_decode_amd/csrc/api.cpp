@@ -90,18 +90,19 @@ int make_plan(const nvfp4_kv_cache *c, int32_t num_seqs, const int64_t *seq_base
     pl.G = G;
     pl.n_q = n_q;
     pl.R = G * n_q;
-    // Up to 64 rows per KV head go through the decode kernels in one pass; more are cut into
-    // balanced chunks of whole row tiles over the same units: two chunks (up to 128 rows,
-    // wide draft windows) as two launches in a row, more (prefill chunks) side by side as
-    // grid y of one launch, with correspondingly fewer units.
-    pl.chunks = (pl.R + nvfp4::kMaxRows - 1) / nvfp4::kMaxRows;
-    pl.chunk_rows = ((pl.R + pl.chunks - 1) / pl.chunks + 15) / 16 * 16;
+    // Up to 64 rows per KV head go through the decode kernels in one pass; more (wide draft
+    // windows, prefill chunks) are cut into 32-row chunks that run side by side as grid y of
+    // one launch over the same units, with correspondingly fewer units. 32-row chunks run on
+    // the single-wave-per-block kernel: against 64-row chunks on the wave-pair kernel, 96
+    // rows over 131k tokens 107.8 -> 91.2 us, a 1,024-token prefill chunk into 32k tokens
+    // (6,144 rows) 1,342 -> 923 us; 48-row chunks 1,040 us.
+    pl.chunk_rows = pl.R <= nvfp4::kMaxRows ? pl.R : nvfp4::kChunkRows;
     pl.chunks = (pl.R + pl.chunk_rows - 1) / pl.chunk_rows;
     pl.NT = (std::min(pl.chunk_rows, pl.R) + 15) / 16;
     pl.D = c->head_dim;
     // Fill every CU with decode_units_per_cu(NT) units. Splits go greedily to the sequence
     // whose units are currently longest, so ragged batches get near-equal units.
-    const int64_t grid_y = pl.chunks > 2 ? pl.chunks : 1;
+    const int64_t grid_y = pl.chunks;
     const int64_t slots = std::max<int64_t>((int64_t)nvfp4::kCUs * nvfp4::decode_units_per_cu(pl.NT) / grid_y,
                                             (int64_t)num_seqs * pl.Hkv);
     int64_t nsp[nvfp4::kMaxSeqs];
@@ -186,25 +187,17 @@ void fill_decode(nvfp4::DecodeParams &dp, const nvfp4::SplitPlan &pl, const nvfp
     dp.units = pl.units;
 }
 
-// The partial kernel over every row chunk (the same units). Up to two chunks: one launch
-// each, and only the first stores the step's new rows, which the second then reads. More:
-// one launch with the chunks on grid y (the caller has stored the new rows before).
+// The partial kernel over every row chunk: one launch, the chunks on grid y over the same
+// units. Up to kMaxStoreRows rows, the workgroup of each sequence's last unit in every
+// chunk stores the step's new rows before reading them (the chunks store identical bytes,
+// and each workgroup orders its own stores before its loads); above that the caller has
+// stored them with the append kernel.
 hipError_t launch_partials(nvfp4::DecodeParams dp, const nvfp4::SplitPlan &pl, hipStream_t s) {
-    if (pl.chunks > 2) {
-        dp.row0 = 0;
-        dp.Rc = pl.chunk_rows;
-        dp.grid_y = pl.chunks;
-        dp.k_new = dp.v_new = nullptr;
-        return nvfp4::launch_decode_partial(dp, pl.D, pl.NT, s);
-    }
-    for (int r0 = 0; r0 < pl.R; r0 += pl.chunk_rows) {
-        dp.row0 = r0;
-        dp.Rc = std::min(pl.chunk_rows, pl.R - r0);
-        hipError_t e = nvfp4::launch_decode_partial(dp, pl.D, (dp.Rc + 15) / 16, s);
-        if (e != hipSuccess) return e;
-        dp.k_new = dp.v_new = nullptr;
-    }
-    return hipSuccess;
+    dp.row0 = 0;
+    dp.Rc = pl.chunk_rows;
+    dp.grid_y = pl.chunks;
+    if (pl.R > nvfp4::kMaxStoreRows) dp.k_new = dp.v_new = nullptr;
+    return nvfp4::launch_decode_partial(dp, pl.D, pl.NT, s);
 }
 
 int check_decode_common(const float *global_scale, void *workspace, size_t workspace_bytes,
@@ -359,8 +352,8 @@ int nvfp4_decode_step(const nvfp4_kv_cache *cache, const float *global_scale, co
     dp.out = out;
     dp.out_bf16 = out_dtype == NVFP4_OUT_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (pl.chunks > 2) {
-        // Row chunks side by side all read the new rows: store them first (append kernel).
+    if (pl.R > nvfp4::kMaxStoreRows) {
+        // Many row chunks side by side all read the new rows: store them first (append kernel).
         int64_t wp[nvfp4::kMaxSeqs], nn[nvfp4::kMaxSeqs];
         for (int b = 0; b < num_seqs; ++b) {
             wp[b] = seq_len[b] - n_q;
@@ -393,7 +386,7 @@ int nvfp4_decode_step_dev_len(const nvfp4_kv_cache *cache, const float *global_s
         return fail(NVFP4_EINVAL, "k_new and v_new must both be given or both be null");
     if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
         return fail(NVFP4_EINVAL, "k_new and v_new must be 16-byte aligned");
-    if (k_new && pl.chunks > 2)
+    if (k_new && pl.R > nvfp4::kMaxStoreRows)
         return fail(NVFP4_EUNSUPPORTED, "%d query rows per KV head: with lengths in device memory the step "
                     "stores its rows itself only up to 128 rows (append first, pass null k_new/v_new)", pl.R);
     if (!aligned16(q)) return fail(NVFP4_EINVAL, "q must be non-null and 16-byte aligned");

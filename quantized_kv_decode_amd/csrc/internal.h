@@ -8,7 +8,9 @@
 namespace nvfp4 {
 
 constexpr int kMaxSeqs = 8;
-constexpr int kMaxRows = 64;
+constexpr int kMaxRows = 64;       // query rows per KV head one decode launch serves per chunk
+constexpr int kChunkRows = 32;     // above kMaxRows: row chunks of this size side by side
+constexpr int kMaxStoreRows = 128; // up to this many rows the decode kernels store a step's rows
 constexpr int kBlockTokens = 32;     // tokens per KV block: one PV MFMA K-step (16x16x32)
 constexpr int kWaves = 4;            // waves per decode workgroup (256 threads)
 constexpr int kCUs = 256;            // compute units the split plan fills (MI355X)
@@ -38,7 +40,7 @@ constexpr int decode_units_per_cu(int NT) { return NT == 2 ? 2 : 1; }
 struct SplitPlan {
     int32_t B, Hkv, Hq, G, n_q, R, NT, D;
     int32_t chunk_rows;                  // rows per row chunk (the last may have fewer)
-    int32_t chunks;                      // row chunks; above 2 they run side by side (grid y)
+    int32_t chunks;                      // row chunks, side by side on grid y (1: R <= 64)
     int32_t n_split[kMaxSeqs];
     int32_t split_len[kMaxSeqs];
     int32_t unit_base[kMaxSeqs];

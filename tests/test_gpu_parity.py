@@ -103,13 +103,13 @@ DECODE_SHAPES = [
     dict(seq_lens=(257,), num_kv_heads=1, num_q_heads=8, head_dim=128, n_q=6),                            # 48 rows
     dict(seq_lens=(1500, 45), num_kv_heads=2, num_q_heads=8, head_dim=128, n_q=5),                        # 20 rows, D 128
     dict(seq_lens=(1234,), num_kv_heads=2, num_q_heads=16, head_dim=256, n_q=4, outlier_frac=0.02),      # 32 rows
-    # wide draft windows: two row chunks over one split plan
-    dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=16),   # 96 rows: 48 + 48
-    dict(seq_lens=(900, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=12, v_dist="laplace"),  # 72: 48 + 24
-    dict(seq_lens=(600,), num_kv_heads=1, num_q_heads=16, head_dim=128, n_q=8),         # 128 rows: 64 + 64
+    # wide draft windows: 32-row chunks side by side over one split plan
+    dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=16),   # 96 rows: 3 chunks
+    dict(seq_lens=(900, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=12, v_dist="laplace"),  # 72: 32 + 32 + 8
+    dict(seq_lens=(600,), num_kv_heads=1, num_q_heads=16, head_dim=128, n_q=8),         # 128 rows: 4 chunks
     dict(seq_lens=(17, 90), num_kv_heads=1, num_q_heads=5, head_dim=256, n_q=15),      # 75 rows, lengths < 2 blocks
-    # prefill chunks: many row chunks side by side, each skipping keys its rows cannot see
-    dict(seq_lens=(600,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=64),        # 384 rows: 6 chunks
+    # prefill chunks: many 32-row chunks side by side, each skipping keys its rows cannot see
+    dict(seq_lens=(600,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=64),        # 384 rows: 12 chunks
     dict(seq_lens=(300, 1000), num_kv_heads=2, num_q_heads=8, head_dim=128, n_q=100),  # 400 rows, ragged
     dict(seq_lens=(2100,), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=256, v_dist="laplace"),  # 1536 rows
 ]
@@ -208,7 +208,7 @@ DEV_LEN_CASES = [
     (dict(seq_lens=(963,), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6, outlier_frac=0.02), 5000),
     (dict(seq_lens=(6, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6), 100000),     # nearly all units empty
     (dict(seq_lens=(9, 20), num_kv_heads=1, num_q_heads=4, head_dim=256, n_q=1), 60000),      # one row tile, same
-    (dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=16), 2000),  # 96 rows, two chunks
+    (dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=16), 2000),  # 96 rows, three chunks
 ]
 
 
