@@ -63,6 +63,13 @@ __device__ inline float max8(const float (&x)[8]) {
     return r;
 }
 
+__device__ inline float max4(const float (&x)[4]) {
+    float a, r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(a) : "v"(x[0]), "v"(x[1]), "v"(x[2]));
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(x[3]));
+    return r;
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer over one head plane: loads past its end return zeros (no fault).

@@ -213,10 +213,15 @@ void decode_pair_kernel(DecodeParams p) {
     float4_t lsum[NT];       // wave 0 of the pair: P . 1 over the same rows
     float m[NT];             // pair-wide reference of row 16 rt + n (base 2)
     float thr[NT];           // m + kPairLazy: a score above it moves the reference
+    // -m, or 0 while m = -inf (the exponent offset of P); kept at three row tiles, formed per
+    // block at four (where NT more live registers would spill)
+    constexpr bool kKeepNmu = NT < 4;
+    float nmu[kKeepNmu ? NT : 1];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
         m[rt] = -INFINITY;
         thr[rt] = -INFINITY;
+        if constexpr (kKeepNmu) nmu[rt] = 0.0f;
         lsum[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < HT; ++t) acc[rt][t] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -239,17 +244,21 @@ void decode_pair_kernel(DecodeParams p) {
     // lim: offset limit of the block relative to L - n_q (32-bit: tokens < 2^31).
     const int lim0 = (int)(un.L - p.n_q - un.t0) - kBlockTokens * pair;
     const int iters = max((nblk + kPairs - 1) / kPairs, 1);   // an empty unit runs one masked trip
+    // Raw MFMA scores of this wave's 16 tokens (masked: -inf). The score factor c is
+    // positive (q_store), so the lane's maximum scaled score is c times max4(x).
     float x[NT][4];
 
-    // fp16 probabilities of this wave's 16 tokens of block j, relative to m, into LDS
+    // fp16 probabilities P = 2^(c s - m) of this wave's 16 tokens of block j into LDS
     auto write_p = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
-            const float mu = m[rt] == -INFINITY ? 0.0f : m[rt];
-            const half2_t p01 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][0] - mu),
-                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][1] - mu)};
-            const half2_t p23 = half2_t{(_Float16)__builtin_amdgcn_exp2f(x[rt][2] - mu),
-                                        (_Float16)__builtin_amdgcn_exp2f(x[rt][3] - mu)};
+            float nm;
+            if constexpr (kKeepNmu) nm = nmu[rt];
+            else nm = m[rt] == -INFINITY ? 0.0f : -m[rt];
+            const half2_t p01 = half2_t{(_Float16)__builtin_amdgcn_exp2f(fmaf(x[rt][0], cexp[rt], nm)),
+                                        (_Float16)__builtin_amdgcn_exp2f(fmaf(x[rt][1], cexp[rt], nm))};
+            const half2_t p23 = half2_t{(_Float16)__builtin_amdgcn_exp2f(fmaf(x[rt][2], cexp[rt], nm)),
+                                        (_Float16)__builtin_amdgcn_exp2f(fmaf(x[rt][3], cexp[rt], nm))};
             uint32_t *dst = reinterpret_cast<uint32_t *>(&pbuf[pair][j & 1][rt][lane]) + 2 * w;
             typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
             *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{as_u32(p01), as_u32(p23)};
@@ -277,7 +286,7 @@ void decode_pair_kernel(DecodeParams p) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[rt][i] = s[rt][i] * cexp[rt];
+            for (int i = 0; i < 4; ++i) x[rt][i] = s[rt][i];
         if (lim < kBlockTokens - 1) {
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt)
@@ -287,9 +296,7 @@ void decode_pair_kernel(DecodeParams p) {
         }
         bool above = false;
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) above |= x[rt][i] > thr[rt];
+        for (int rt = 0; rt < NT; ++rt) above |= max4(x[rt]) * cexp[rt] > thr[rt];
         write_p(j);
         const uint8_t flag = __builtin_amdgcn_ballot_w64(above) != 0 ? 1 : 0;   // all lanes vote
         if (lane == 0) mflag[j & 1][wave] = flag;
@@ -300,7 +307,7 @@ void decode_pair_kernel(DecodeParams p) {
         float mloc[NT];
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
-            mloc[rt] = wave_max_g(fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3])));
+            mloc[rt] = wave_max_g(max4(x[rt]) * cexp[rt]);
             if (g == 0) xmax[pair][w][16 * rt + n] = mloc[rt];
         }
         __syncthreads();
@@ -314,6 +321,7 @@ void decode_pair_kernel(DecodeParams p) {
             alpha[rt] = need ? exp2f(m[rt] - mnew) : 1.0f;   // m = -inf -> 0
             m[rt] = mnew;
             thr[rt] = mnew + kPairLazy;
+            if constexpr (kKeepNmu) nmu[rt] = mnew == -INFINITY ? 0.0f : -mnew;
             need_any |= need;
         }
         if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
