@@ -477,7 +477,13 @@ void decode_partial_kernel(DecodeParams p) {
 // merged through LDS. Every sum runs in a fixed order, so the result does not depend
 // on timing.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
+// Up to 128 VGPRs (four waves per SIMD; the grid is one workgroup per output row): at the
+// default target of eight waves the compiler held back three of a batch's eight partial
+// loads until the first five had arrived, a second memory round trip. Same box: decode_27b
+// step 24.0 -> 23.3 us; at one wave per SIMD the three-session step got slower instead
+// (261.5 -> 263.5 us; four waves: 261.1).
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(4, 4)))
+void decode_combine_kernel(DecodeParams p) {
     constexpr int PER = D / 64;                       // outputs per lane
     typedef float vecf __attribute__((ext_vector_type(PER)));
     const int R = p.R;
@@ -488,6 +494,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     const int ns = p.n_split[b];
     const int64_t u0 = (int64_t)p.unit_base[b] + (int64_t)kh * ns;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const float *gvp = p.gscale + (b * p.Hkv + kh) * 2 + 1;
+    const int i = r / p.G, h = kh * p.G + (r - i * p.G);
+    const int64_t idx = (((int64_t)b * p.n_q + i) * p.Hq + h) * D + PER * lane;
+    uint8_t *const outp = static_cast<uint8_t *>(p.out);
+    const int out_bf16 = p.out_bf16;
     const float *mrow = p.ws_m + u0 * R + r;          // m of unit s at mrow[s * R]
     const float *lrow = p.ws_l + u0 * R + r;
     const float *orow = p.ws_o + (u0 * R + r) * D + PER * lane;
@@ -498,9 +509,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     // scalar loads they were issued one after another)
     int vz;
     asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
-    float M = -INFINITY, den = 0.f;
+    float M = -INFINITY, den = 0.f, gv = 0.f;
     vecf acc = {};
     for (int s0 = wave; s0 < ns; s0 += kWaves * BATCH) {
+        // g_V and the output's arguments in the batch's round trip rather than after the
+        // cross-wave merge (wave 0, which writes the output, always runs this loop)
+        gv = gvp[vz];
         float ms[BATCH], ls[BATCH];
         vecf o[BATCH];
 #pragma unroll
@@ -512,6 +526,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
             o[k] = *reinterpret_cast<const vecf *>(orow + sc * R * D);
             if (s >= ns) ms[k] = -INFINITY;
         }
+        asm volatile("" ::"s"(outp), "s"(out_bf16));
         float mb = ms[0];
 #pragma unroll
         for (int k = 1; k < BATCH; ++k) mb = fmaxf(mb, ms[k]);
@@ -548,18 +563,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
             dd += f * dpart[w];
         }
         // v_hat = (e2m1 * S * 2^-8) * 2^8 * g_V
-        o *= 256.0f * p.gscale[(b * p.Hkv + kh) * 2 + 1] / dd;
-        const int i = r / p.G, h = kh * p.G + (r - i * p.G);
-        const int64_t idx = (((int64_t)b * p.n_q + i) * p.Hq + h) * D + PER * lane;
-        if (p.out_bf16) {
+        o *= 256.0f * gv / dd;
+        if (out_bf16) {
             // IEEE conversion: round to nearest even (v_cvt_pk_bf16_f32)
             typedef __bf16 vecb __attribute__((ext_vector_type(PER)));
             vecb ob;
 #pragma unroll
             for (int k = 0; k < PER; ++k) ob[k] = (__bf16)o[k];
-            *reinterpret_cast<vecb *>(reinterpret_cast<__bf16 *>(p.out) + idx) = ob;
+            *reinterpret_cast<vecb *>(reinterpret_cast<__bf16 *>(outp) + idx) = ob;
         } else {
-            *reinterpret_cast<vecf *>(reinterpret_cast<float *>(p.out) + idx) = o;
+            *reinterpret_cast<vecf *>(reinterpret_cast<float *>(outp) + idx) = o;
         }
     }
 }
