@@ -486,11 +486,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void decode_combine_kernel(DecodeParams p) {
     constexpr int PER = D / 64;                       // outputs per lane
     typedef float vecf __attribute__((ext_vector_type(PER)));
+    // grid (R, Hkv, B): the indices need no kernel argument, so the per-sequence arguments
+    // below are loaded in the kernel's first round of scalar loads
     const int R = p.R;
-    const int blk = blockIdx.x;
-    const int r = blk % R;
-    const int bk = blk / R;
-    const int kh = bk % p.Hkv, b = bk / p.Hkv;
+    const int r = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
     const int ns = p.n_split[b];
     const int64_t u0 = (int64_t)p.unit_base[b] + (int64_t)kh * ns;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -596,7 +595,7 @@ hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream
 }
 
 hipError_t launch_decode_combine(const DecodeParams &p, int D, hipStream_t s) {
-    const unsigned blocks = (unsigned)(p.B * p.Hkv * p.R);
+    const dim3 blocks((unsigned)p.R, (unsigned)p.Hkv, (unsigned)p.B);
     if (D == 256)
         hipLaunchKernelGGL(decode_combine_kernel<256>, dim3(blocks), dim3(256), 0, s, p);
     else if (D == 128)
