@@ -510,7 +510,18 @@ void decode_combine_kernel(DecodeParams p) {
     asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
     float M = -INFINITY, den = 0.f, gv = 0.f;
     vecf acc = {};
-    for (int s0 = wave; s0 < ns; s0 += kWaves * BATCH) {
+    if (ns <= kWaves) {
+        // at most one unit per wave (long query chunks split into few units): that unit's
+        // loads alone, not a batch of copies of it
+        gv = gvp[vz];
+        if (wave < ns) {
+            M = mrow[(int64_t)wave * R + vz];
+            den = lrow[(int64_t)wave * R + vz];
+            acc = *reinterpret_cast<const vecf *>(orow + (int64_t)wave * R * D);
+        }
+        asm volatile("" ::"s"(outp), "s"(out_bf16));
+    }
+    for (int s0 = wave; ns > kWaves && s0 < ns; s0 += kWaves * BATCH) {
         // g_V and the output's arguments in the batch's round trip rather than after the
         // cross-wave merge (wave 0, which writes the output, always runs this loop)
         gv = gvp[vz];
