@@ -209,6 +209,9 @@ DEV_LEN_CASES = [
     (dict(seq_lens=(6, 40), num_kv_heads=1, num_q_heads=6, head_dim=256, n_q=6), 100000),     # nearly all units empty
     (dict(seq_lens=(9, 20), num_kv_heads=1, num_q_heads=4, head_dim=256, n_q=1), 60000),      # one row tile, same
     (dict(seq_lens=(700, 129), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=16), 2000),  # 96 rows, three chunks
+    # 128 rows in 4 chunks: bounds of 500 / 415 tokens plan 3 units per sequence, most of them
+    # empty at these lengths, and the combine takes its path for at most one unit per wave
+    (dict(seq_lens=(130, 45), num_kv_heads=1, num_q_heads=16, head_dim=128, n_q=8), 370),
 ]
 
 
