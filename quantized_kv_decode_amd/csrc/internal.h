@@ -92,7 +92,7 @@ struct CalibParams {
 
 hipError_t launch_calibrate(const CalibParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
-// NT == 1: four waves per block stream; NT 2..4: the wave-pair kernel.
+// NT 1..2: the four waves take alternate blocks; NT 3..4: the wave-pair kernel.
 hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream_t s);
 hipError_t launch_decode_pair(const DecodeParams &p, int D, int NT, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeParams &p, int D, hipStream_t s);

@@ -123,7 +123,7 @@ WORKLOADS = {
         "append_max_context", 5, (600000,), 4, 24, 256, 1, append_rows=8192,
         description="append an 8192-row prefill chunk into a 600000-token cache, then decode over all 600000"),
     # not one of the five configurations: a wide draft window (DFlash-style, 1 + 15 drafts),
-    # 96 query rows per KV head, which the decode path serves in two row chunks
+    # 96 query rows per KV head, which the decode path serves as three 32-row chunks side by side
     "dflash_verify": Workload(
         "dflash_verify", 6, (131072,), 4, 24, 256, 16, outlier_frac=0.02,
         description="wide draft verify: 1 x 131072, 16 query tokens (1 + 15 drafts) causal, 2% channels x20"),
