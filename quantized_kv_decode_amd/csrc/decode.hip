@@ -290,7 +290,6 @@ struct Lds {
 template <int D, int NT, bool DevLen>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_waves_per_simd(NT))))
 void decode_partial_kernel(DecodeParams p) {
-    constexpr int KK = D / 32;
     constexpr int EPL = D / 16;
     using LD = Lds<D, NT>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LD::BYTES];
@@ -456,7 +455,7 @@ void decode_partial_kernel(DecodeParams p) {
         }
         __syncthreads();
     }
-    if (threadIdx.x < R) {
+    if ((int)threadIdx.x < R) {
         const int row = threadIdx.x;
         float M = -INFINITY;
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][row]);

@@ -453,7 +453,7 @@ void decode_pair_kernel(DecodeParams p) {
             }
         }
     }
-    if (threadIdx.x < R) {
+    if ((int)threadIdx.x < R) {
         const int row = threadIdx.x;
         float M = sm_m[0][row];
 #pragma unroll
