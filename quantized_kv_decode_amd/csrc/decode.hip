@@ -475,12 +475,12 @@ void decode_partial_kernel(DecodeParams p) {
 // owns the D/64 contiguous outputs [c D/64, (c + 1) D/64). The four wave results are
 // merged through LDS. Every sum runs in a fixed order, so the result does not depend
 // on timing.
+// Built for up to 128 VGPRs (four waves per SIMD; the grid is one workgroup per output
+// row): at the default target of eight waves the compiler held back three of a batch's
+// eight partial loads until the first five had arrived, a second memory round trip. Same
+// box: decode_27b step 24.0 -> 23.3 us; at one wave per SIMD the three-session step got
+// slower instead (261.5 -> 263.5 us; four waves: 261.1).
 template <int D>
-// Up to 128 VGPRs (four waves per SIMD; the grid is one workgroup per output row): at the
-// default target of eight waves the compiler held back three of a batch's eight partial
-// loads until the first five had arrived, a second memory round trip. Same box: decode_27b
-// step 24.0 -> 23.3 us; at one wave per SIMD the three-session step got slower instead
-// (261.5 -> 263.5 us; four waves: 261.1).
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(4, 4)))
 void decode_combine_kernel(DecodeParams p) {
     constexpr int PER = D / 64;                       // outputs per lane
