@@ -238,13 +238,14 @@ def test_decode_step_device_lengths(qk, shape, extra):
     _check_decode(w, ref, out)
 
 
-@pytest.mark.parametrize("n_q", [1, 4])
+@pytest.mark.parametrize("n_q", [1, 4, 16])
 def test_decode_step_device_lengths_graph_replay(qk, n_q):
     """One HIP graph of the device-length step, captured once and replayed over four decode
     steps while the sequences grow by n_q tokens per step (new q, k_new, v_new and lengths
     written into the same buffers between replays): every replay passes the oracle at its
     lengths, the pool matches the oracle's bytes at the end, and replaying the last step
-    again gives identical output bits."""
+    again gives identical output bits. n_q = 16 is 96 rows per KV head: three 32-row chunks
+    side by side, each storing the step's rows itself."""
     w = workloads.small(seq_lens=(1500, 333), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=n_q)
     say("graph replay, device lengths, n_q", n_q)
     ref = OracleRun(w)
