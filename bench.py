@@ -68,42 +68,90 @@ def read_traffic(workload: str):
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
-    """The fp64 oracle timed on the host on a bounded sample of the same workload:
-    repeated decode steps (quantise the n_q new rows, attention for every query row)
-    over the full cache until about budget_s seconds have elapsed."""
+    """The fp64 oracle timed on the host on a bounded sample of the same workload: the decode
+    step (quantise the n_q new K/V rows, then attention for every query row) of the first
+    sequence's first KV heads, each over that sequence's whole cache, repeated until about
+    budget_s seconds have passed. The rate is the sample's packed KV bytes per step over the
+    time per step (the unit of the GPU figure); a second, single-thread leg times the rows
+    of one query token of one KV head."""
     import numpy as np
     import oracle
     import workloads
     nthreads = oracle.default_threads()
-    k = workloads.all_kv_rows(w, "k")
-    v = workloads.all_kv_rows(w, "v")
-    ku, vu = workloads.as_u16(k), workloads.as_u16(v)
-    g = oracle.calibrate(ku, vu, w.seq_lens)
-    cache = oracle.Cache(w.num_kv_heads, w.head_dim, w.capacity)
-    oracle.append(cache, ku, vu, g, w.seq_base, [0] * w.batch, list(w.seq_lens), nthreads)
-    q = workloads.as_u16(workloads.queries(w))
-    rows = [r for b in range(w.batch) for r in range(w.seq_base[b] + w.seq_lens[b] - w.n_q,
-                                                     w.seq_base[b] + w.seq_lens[b])]
-    kn, vn = np.ascontiguousarray(ku[rows]), np.ascontiguousarray(vu[rows])
-    wp = [L - w.n_q for L in w.seq_lens]
+    b, L = 0, w.seq_lens[0]
+    heads = list(range(min(2, w.num_kv_heads)))
+    q_all = workloads.as_u16(workloads.queries(w))
+    k_rows = workloads.as_u16(workloads.kv_rows(w, "k", b))
+    v_rows = workloads.as_u16(workloads.kv_rows(w, "v", b))
+    parts = []
+    for kh in heads:                         # one single-head cache per sampled KV head
+        ku = np.ascontiguousarray(k_rows[:, kh:kh + 1])
+        vu = np.ascontiguousarray(v_rows[:, kh:kh + 1])
+        g = oracle.calibrate(ku, vu, [L])
+        cache = oracle.Cache(1, w.head_dim, L)
+        oracle.append(cache, ku, vu, g, [0], [0], [L - w.n_q], nthreads)
+        q = np.ascontiguousarray(q_all[b:b + 1, :, kh * w.group:(kh + 1) * w.group])
+        kn, vn = np.ascontiguousarray(ku[L - w.n_q:]), np.ascontiguousarray(vu[L - w.n_q:])
+        parts.append((cache, g, q, kn, vn))
+    del k_rows, v_rows
+
+    def step(cache, g, q, kn, vn, nth, sel=None):
+        oracle.append(cache, kn, vn, g, [0], [L - w.n_q], [w.n_q], nth)
+        oracle.attention(cache, g, q, [0], [L], w.n_q, w.sm_scale, sel=sel, nthreads=nth)
+
     steps, t0 = 0, time.perf_counter()
     while True:
-        oracle.append(cache, kn, vn, g, w.seq_base, wp, [w.n_q] * w.batch, nthreads)
-        oracle.attention(cache, g, q, w.seq_base, w.seq_lens, w.n_q, w.sm_scale, nthreads=nthreads)
+        for pt in parts:
+            step(*pt, nthreads)
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 1000:
             break
-    # one thread, one step (a few seconds at these sizes): the per-core rate
+    bytes_per_step = len(heads) * L * workloads.packed_bytes_per_token_head(w.head_dim)
+    # one thread: the G rows of the first query token of the first sampled head
     t1 = time.perf_counter()
-    oracle.append(cache, kn, vn, g, w.seq_base, wp, [w.n_q] * w.batch, 1)
-    oracle.attention(cache, g, q, w.seq_base, w.seq_lens, w.n_q, w.sm_scale, nthreads=1)
+    step(*parts[0], 1, sel=[(0, 0, h) for h in range(w.group)])
     el1 = time.perf_counter() - t1
-    return {"value": round(w.kv_bytes * steps / el / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"{steps} full decode step(s) of {w.name} (append n_q rows + fp64 attention for all "
-                      f"{w.batch * w.n_q * w.num_q_heads} query rows over the whole cache), {el:.1f} s",
-            "ms_per_step": round(el / steps * 1e3, 3),
-            "single_thread_ms_per_step": round(el1 * 1e3, 3), "cpu_model": cpu_model()}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return {"value": round(bytes_per_step * steps / el / 1e9, 4), "unit": "GB/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{steps} decode step(s) of {w.name}'s sequence 0 ({L} tokens), KV heads {heads}: append "
+                      f"the {w.n_q} new rows + fp64 attention for all {w.group * w.n_q} query rows of each head "
+                      f"over the whole sequence, {el:.1f} s; value = sampled packed KV bytes per step / time",
+            "ms_per_step": round(el / steps * 1e3, 3), "threads": nthreads, "nproc": os.cpu_count(),
+            "affinity_cpus": affinity,
+            "single_thread": {"rows": w.group, "keys_per_row": L - w.n_q + 1, "ms": round(el1 * 1e3, 3),
+                              "GBps": round(L * workloads.packed_bytes_per_token_head(w.head_dim) / el1 / 1e9
+                                            * w.group / (w.group * w.n_q), 4)},
+            "cpu_model": cpu_model()}
+
+
+def hbm_probe(dev, nbytes: int = 1 << 30):
+    """Best plain streaming read rate (GB/s) over a few launch sizes of the library's read
+    probe, each timed over 10 launches between events."""
+    import torch
+    import quantized_kv_decode_amd as qk
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(16384, dtype=torch.int32, device=dev)
+    s = torch.cuda.current_stream()
+    best, rates = 0.0, {}
+    for wg in (1024, 2048, 4096, 8192, 16384):
+        for _ in range(3):
+            qk.hbm_read_probe(buf, wg, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(10):
+            qk.hbm_read_probe(buf, wg, sink)
+        e1.record(s)
+        e1.synchronize()
+        gbps = nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        rates[wg] = round(gbps, 1)
+        best = max(best, gbps)
+    del buf, sink
+    return best, rates
 
 
 def cpu_model() -> str:
@@ -121,7 +169,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_27b")
+    ap.add_argument("--workload", default="long_agentic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -313,6 +361,8 @@ def main() -> int:
     if dev_len:
         assert (out_dl - out).abs().max().item() <= 1e-4 * out.abs().max().item(), "device-length step disagrees"
 
+    log("read probe")
+    achievable, probe_rates = hbm_probe(dev)
     kv = w.kv_bytes
     achieved = kv / (ms_part * 1e-3) / 1e9
     traffic = read_traffic(w.name)
@@ -351,6 +401,11 @@ def main() -> int:
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_partial", "algorithmic_bytes_per_launch": kv},
     }
+    step_gbps = kv / (ms_step * 1e-3) / 1e9
+    res["achievable"] = {"GBps": round(achievable, 1), "step_frac": round(step_gbps / achievable, 4),
+                         "partial_frac": round(achieved / achievable, 4),
+                         "probe": "plain streaming read of 1 GiB, 16-byte loads (nvfp4_hbm_read_probe), best of "
+                                  "these workgroup counts", "by_workgroups": probe_rates}
     res["device_lengths_step_us"] = round(ms_dl * 1e3, 3) if dev_len else None
     res["step_us_spread"] = spread
     res["stream_launch_step_us"] = round(eager_us, 3)

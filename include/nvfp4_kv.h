@@ -199,6 +199,16 @@ int nvfp4_decode_attn_combine(const nvfp4_kv_cache *cache, const float *global_s
                               const int64_t *seq_len, int32_t n_q, int32_t num_q_heads,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Streaming-read probe (measurement only, not part of the decode path): reads `bytes` of
+ * device memory at `buf` once with 16-byte loads from `workgroups` 256-thread workgroups and
+ * writes one fold of the data per workgroup to sink[0 .. workgroups). Timing it gives the
+ * read rate a plain streaming kernel reaches, the practical ceiling for the decode kernels
+ * (knoopx/ninfer page, "Quick start": the engine ships a standalone HBM probe).
+ *   buf:  device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink: device uint32 [workgroups], 4-byte aligned; contents are a checksum, not a result
+ * Errors: EINVAL (pointers, bytes, workgroups outside [1, 65536]). */
+int nvfp4_hbm_read_probe(const void *buf, size_t bytes, void *sink, int32_t workgroups, void *stream);
+
 /* Message describing the last failure on this thread ("" if none). */
 const char *nvfp4_last_error(void);
 

@@ -29,7 +29,8 @@ _ERR_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ERANGE: "ERANGE",
               EWORKSPACE: "EWORKSPACE", EHIP: "EHIP"}
 
 SYMBOLS = ["nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn_workspace_bytes",
-           "nvfp4_decode_attn", "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine",
+           "nvfp4_decode_attn", "nvfp4_decode_step", "nvfp4_decode_step_dev_len",
+           "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine", "nvfp4_hbm_read_probe",
            "nvfp4_last_error"]
 
 
@@ -69,10 +70,12 @@ def load_library():
                                               vp]
     lib.nvfp4_decode_attn_partial.argtypes = [P, vp, vp, i32, i64, i64, i32, i32, f32, vp, sz, vp]
     lib.nvfp4_decode_attn_combine.argtypes = [P, vp, vp, i32, i32, i64, i32, i32, vp, sz, vp]
+    lib.nvfp4_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_last_error.restype = ctypes.c_char_p
     for f in ("nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn", "nvfp4_decode_step",
-              "nvfp4_decode_step_dev_len", "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine"):
+              "nvfp4_decode_step_dev_len", "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine",
+              "nvfp4_hbm_read_probe"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -118,7 +121,7 @@ class KVPool:
 
     @property
     def nbytes(self) -> int:
-        return sum(t.numel() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
+        return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
 
     def desc(self) -> CacheDesc:
         return CacheDesc(self.k_codes.data_ptr(), self.k_scales.data_ptr(), self.v_codes.data_ptr(),
@@ -230,3 +233,13 @@ def decode_attn_combine(pool: KVPool, global_scale, out, seq_len, workspace, str
     _check(load_library().nvfp4_decode_attn_combine(ctypes.byref(d), _ptr(global_scale), _ptr(out), code, B,
                                                     _i64(seq_len), n_q, Hq, _ptr(workspace), workspace.numel(),
                                                     _stream(stream)))
+
+
+def hbm_read_probe(buf: torch.Tensor, workgroups: int, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Streaming-read probe over the bytes of `buf` (device, 16-byte aligned, size a multiple of 16);
+    returns the sink (uint32 [workgroups], a checksum). Timing it gives the plain streaming read rate."""
+    if sink is None:
+        sink = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().nvfp4_hbm_read_probe(_ptr(buf), nbytes, _ptr(sink), int(workgroups), _stream(stream)))
+    return sink

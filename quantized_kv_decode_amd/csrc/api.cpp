@@ -14,10 +14,11 @@
 #include "nvfp4_kv.h"
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-int fail(int code, const char *fmt, ...) {
+namespace nvfp4 {
+int report_error(int code, const char *fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -26,6 +27,11 @@ int fail(int code, const char *fmt, ...) {
     g_last_error = buf;
     return code;
 }
+}  // namespace nvfp4
+
+namespace {
+
+int (*const fail)(int, const char *, ...) = &nvfp4::report_error;
 
 int ok() {
     g_last_error.clear();
@@ -121,6 +127,10 @@ int make_plan(const nvfp4_kv_cache *c, int32_t num_seqs, const int64_t *seq_base
         nsp[best] += 1;
         total += pl.Hkv;
     }
+    // No unit longer than kMaxUnitTokens (the fp16 probability floor, see internal.h), even if
+    // that takes more units than resident workgroup slots (very many sequence x head pairs).
+    for (int b = 0; b < num_seqs; ++b)
+        nsp[b] = std::max<int64_t>(nsp[b], (seq_len[b] + nvfp4::kMaxUnitTokens - 1) / nvfp4::kMaxUnitTokens);
     int32_t ub = 0;
     for (int b = 0; b < num_seqs; ++b) {
         int64_t len = (seq_len[b] + nsp[b] - 1) / nsp[b];
@@ -430,6 +440,17 @@ int nvfp4_decode_attn(const nvfp4_kv_cache *cache, const float *global_scale, co
     hipError_t e = launch_partials(dp, pl, s);
     if (e != hipSuccess) return hip_status(e, "decode partial launch");
     return hip_status(nvfp4::launch_decode_combine(dp, pl.D, s), "decode combine launch");
+}
+
+int nvfp4_hbm_read_probe(const void *buf, size_t bytes, void *sink, int32_t workgroups, void *stream) {
+    if (!aligned16(buf)) return fail(NVFP4_EINVAL, "buf must be non-null and 16-byte aligned");
+    if (bytes < 16 || bytes % 16 != 0) return fail(NVFP4_EINVAL, "bytes must be a positive multiple of 16");
+    if (!sink || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+        return fail(NVFP4_EINVAL, "sink must be non-null and 4-byte aligned");
+    if (workgroups < 1 || workgroups > 65536) return fail(NVFP4_EINVAL, "workgroups must be in [1, 65536]");
+    return hip_status(nvfp4::launch_read_probe(buf, bytes, static_cast<uint32_t *>(sink), workgroups,
+                                               static_cast<hipStream_t>(stream)),
+                      "read probe launch");
 }
 
 }  // extern "C"

@@ -136,6 +136,10 @@ __device__ inline Unit unit_of(const DecodeParams &p, int u) {
         const int Ld = __builtin_amdgcn_readfirstlane((int)min(max(p.len_dev[r.b], (int64_t)p.n_q), p.seq_len[r.b]));
         const int L = Ld;
         int sl = (L + ns - 1) / ns;
+        // At least n_q tokens per unit: with a short length over many planned units the
+        // step's n_q new rows would otherwise reach into the unit before the last one, whose
+        // workgroup would read slots that the last unit's workgroup is storing.
+        sl = max(sl, p.n_q);
         sl = (sl + kBlockTokens - 1) / kBlockTokens * kBlockTokens;
         int ne = (L + sl - 1) / sl;
         if (ne > 1 && L - (ne - 1) * sl < p.n_q) ne -= 1;    // the newest n_q tokens stay in one unit

@@ -14,6 +14,12 @@ constexpr int kMaxStoreRows = 128; // up to this many rows the decode kernels st
 constexpr int kBlockTokens = 32;     // tokens per KV block: one PV MFMA K-step (16x16x32)
 constexpr int kWaves = 4;            // waves per decode workgroup (256 threads)
 constexpr int kCUs = 256;            // compute units the split plan fills (MI355X)
+// Longest unit the split planner makes. Probabilities enter the PV product in fp16 against
+// the running reference of one wave (or wave pair); a weight below 2^-25 of that reference
+// rounds to 0 (below 2^-14 it keeps only absolute precision 2^-25). A wave sees at most a
+// quarter of a unit, so this caps the mass lost to that floor at 8192 x 2^-24 (about 4.9e-4)
+// of the output's V range, next to the 2^-10 bound of fp16 rounding in the normal range.
+constexpr int kMaxUnitTokens = 32768;
 
 // Waves per SIMD that the partial kernel for NT row tiles is built for, set by its register
 // budget: two everywhere (one or two row tiles: the single-wave-per-block kernel, up to 256
@@ -90,11 +96,15 @@ struct CalibParams {
     int64_t row_start[kMaxSeqs + 1];
 };
 
+// Records the thread's last error message (nvfp4_last_error) and returns code.
+int report_error(int code, const char *fmt, ...);
+
 hipError_t launch_calibrate(const CalibParams &p, hipStream_t s);
 hipError_t launch_append(const AppendParams &p, hipStream_t s);
 // NT 1..2: the four waves take alternate blocks; NT 3..4: the wave-pair kernel.
 hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream_t s);
 hipError_t launch_decode_pair(const DecodeParams &p, int D, int NT, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeParams &p, int D, hipStream_t s);
+hipError_t launch_read_probe(const void *buf, uint64_t bytes, uint32_t *sink, int workgroups, hipStream_t s);
 
 }  // namespace nvfp4

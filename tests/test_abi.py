@@ -32,8 +32,26 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn_workspace_bytes", "nvfp4_decode_attn",
               "nvfp4_decode_step", "nvfp4_decode_step_dev_len", "nvfp4_decode_attn_partial",
-              "nvfp4_decode_attn_combine", "nvfp4_last_error"):
+              "nvfp4_decode_attn_combine", "nvfp4_hbm_read_probe", "nvfp4_last_error"):
         assert f in names
+
+
+def test_binding_symbol_list_matches_header():
+    import quantized_kv_decode_amd as qk
+    assert sorted(qk.SYMBOLS) == declared_functions()
+
+
+def test_read_probe_validation_codes(lib):
+    import quantized_kv_decode_amd as qk
+    a, sink = 0x100000, 0x200000
+    assert lib.nvfp4_hbm_read_probe(0, 1024, sink, 4, None) == qk.EINVAL
+    assert lib.nvfp4_hbm_read_probe(a + 8, 1024, sink, 4, None) == qk.EINVAL
+    assert lib.nvfp4_hbm_read_probe(a, 1000, sink, 4, None) == qk.EINVAL      # not a multiple of 16
+    assert lib.nvfp4_hbm_read_probe(a, 0, sink, 4, None) == qk.EINVAL
+    assert lib.nvfp4_hbm_read_probe(a, 1024, 0, 4, None) == qk.EINVAL
+    assert lib.nvfp4_hbm_read_probe(a, 1024, sink + 2, 4, None) == qk.EINVAL
+    assert lib.nvfp4_hbm_read_probe(a, 1024, sink, 0, None) == qk.EINVAL
+    assert lib.nvfp4_hbm_read_probe(a, 1024, sink, 65537, None) == qk.EINVAL
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -193,8 +211,11 @@ def test_prefill_rows_plan_fewer_units(lib):
     d = _desc(qk, cap=10 ** 6)
     al = lambda x: (x + 255) // 256 * 256
     R = 6 * 1024
-    got = lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([40000]), 1024, 24)
+    got = lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([30000]), 1024, 24)
     assert got == al(4 * R * 256 * 4) + 2 * al(4 * R * 4)
+    # past the 32768-token unit cap each head's sequence takes two units
+    got = lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([40000]), 1024, 24)
+    assert got == al(8 * R * 256 * 4) + 2 * al(8 * R * 4)
 
 
 def test_split_plan_last_unit_holds_new_rows(lib):
@@ -213,3 +234,20 @@ def test_split_plan_last_unit_holds_new_rows(lib):
     assert ws(4003, 3) == expected(26 * 4, 6 * 3)        # remainder 3 >= n_q: its own unit
     assert ws(4003, 4) == expected(25 * 4, 6 * 4)        # remainder 3 < n_q: merged
     assert ws(4003, 6) == expected(25 * 4, 6 * 6)
+
+
+def test_split_plan_caps_unit_length(lib):
+    """No unit is longer than 32768 tokens, even when that takes more units than the 256
+    workgroup slots of a one-row-tile launch: with 8 sequences x 32 KV heads (one unit per
+    (sequence, head) fills the slots) at 200000 tokens each, every (sequence, head) is cut
+    into ceil(200000 / 32768) = 7 units of 28576 tokens (a multiple of 32)."""
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk, H=32, D=128, cap=8 * 200000)
+    al = lambda x: (x + 255) // 256 * 256
+    lens = [200000] * 8
+    got = lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 8, qk._i64(lens), 1, 32)
+    units = 8 * 32 * 7
+    assert got == al(units * 1 * 128 * 4) + 2 * al(units * 1 * 4)
+    # at or below the cap nothing changes: one unit per (sequence, head)
+    got = lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 8, qk._i64([32768] * 8), 1, 32)
+    assert got == al(256 * 128 * 4) + 2 * al(256 * 4)

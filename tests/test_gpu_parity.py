@@ -212,6 +212,15 @@ DEV_LEN_CASES = [
     # 128 rows in 4 chunks: bounds of 500 / 415 tokens plan 3 units per sequence, most of them
     # empty at these lengths, and the combine takes its path for at most one unit per wave
     (dict(seq_lens=(130, 45), num_kv_heads=1, num_q_heads=16, head_dim=128, n_q=8), 370),
+    # many query tokens against a bound far above the length: the device splits a short
+    # length over many planned units, and every unit must still hold at least n_q tokens so
+    # that the step's new rows all fall in the last one (one-wave kernel at 32 rows, the pair
+    # kernel at 48 and 64, row chunks at 96 and 128)
+    (dict(seq_lens=(200, 77), num_kv_heads=1, num_q_heads=1, head_dim=256, n_q=32), 60000),
+    (dict(seq_lens=(300, 97), num_kv_heads=1, num_q_heads=1, head_dim=256, n_q=48), 100000),
+    (dict(seq_lens=(300,), num_kv_heads=2, num_q_heads=2, head_dim=128, n_q=64), 100000),
+    (dict(seq_lens=(250, 140), num_kv_heads=1, num_q_heads=2, head_dim=256, n_q=48), 50000),
+    (dict(seq_lens=(400,), num_kv_heads=1, num_q_heads=1, head_dim=128, n_q=128), 80000),
 ]
 
 
@@ -348,6 +357,47 @@ def test_extreme_scores_and_constant_v(qk):
     assert torch.allclose(o[:, :, 4:], torch.full_like(o[:, :, 4:], -0.75), rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("n_q", [1, 36])
+def test_fp16_probability_floor_long_units(qk, n_q):
+    """Probabilities enter the PV product in fp16 against a wave's running reference, so a
+    weight below 2^-25 of it rounds to 0. Here every (sequence, KV head) has one key 17.5 nats
+    above a flat tail of ~200,000 keys whose V differs from that key's (-1 against +1): each
+    tail key's weight rounds to 0 in the wave that holds the dominant key. With one unit per
+    (sequence, head) -- 8 sequences x 32 KV heads fill the 256 slots -- that wave would see
+    50,000 keys and lose 2.5e-3 of the V range; the planner's 32,768-token unit cap keeps it
+    at a quarter of that. The expected output has a closed form (K and V bytes written
+    directly): o = (-e^s + N) / (e^s + N) in every element, N the visible tail keys.
+    n_q = 1 runs the one-wave kernel, n_q = 36 (36 rows) the pair kernel."""
+    B, Hkv, D, L = 8, 32, 128, 200000
+    Hq = Hkv
+    say("fp16 probability floor, n_q", n_q)
+    cap = B * L
+    pool = qk.KVPool(Hkv, D, cap, device="cuda")
+    base = [b * L for b in range(B)]
+    pool.v_codes.fill_(0x22)                 # code 2 in both nibbles: +1.0
+    pool.v_scales.fill_(0x38)                # E4M3 1.0
+    for b0 in base:
+        pool.k_codes[:, b0].fill_(0x22)      # the dominant key: k_hat = 1.0 everywhere
+        pool.k_scales[:, b0].fill_(0x38)
+        pool.v_codes[:, b0].fill_(0xAA)      # its V: -1.0
+    g = torch.ones((B, Hkv, 2), dtype=torch.float32, device="cuda")
+    sm = 1.0 / math.sqrt(D)
+    c = 1.546875                             # bf16-exact; s = c * D * sm = 17.5 nats
+    q = torch.full((B, n_q, Hq, D), c, dtype=torch.bfloat16, device="cuda")
+    out = qk.decode_attn(pool, g, q, base, [L] * B, sm)
+    torch.cuda.synchronize()
+    s = c * D * sm
+    got = out.cpu().double()
+    worst = 0.0
+    for i in range(n_q):
+        N = L - n_q + i                      # visible keys 1 .. L - n_q + i
+        exp = (-math.exp(s) + N) / (math.exp(s) + N)
+        worst = max(worst, (got[:, i] - exp).abs().max().item())
+    say(f"  max err {worst:.3e}  tol {TOL_REL:.3e}")
+    assert worst <= TOL_REL * 1.0            # max |V_hat| = 1
+    del pool
+
+
 @pytest.mark.parametrize("scale", [-0.0625, 0.0])
 def test_nonpositive_softmax_scale(qk, scale):
     """A negative softmax scale (the kernels put its sign into the query fragments and keep
@@ -394,51 +444,77 @@ def test_workspace_too_small_is_rejected(qk):
 
 
 # ------------------------------------------------------- full-size workloads ------
-def _sample_rows(w, per_head_rows):
-    rng = np.random.default_rng(w.index)
-    sel = []
-    for b in range(w.batch):
-        for h in range(w.num_q_heads):
-            for i in rng.choice(w.n_q, size=min(per_head_rows, w.n_q), replace=False):
-                sel.append((b, int(i), h))
-    return sel
+def _full_step(qk, w, ref):
+    """The configuration's timed path: the pool filled up to L - n_q per sequence (the
+    max-context workload as its 591,808 rows, then its prefill chunk up to the step's row),
+    then one nvfp4_decode_step -- the call the benchmark times, with the workspace size and
+    split plan it uses -- storing the step's n_q rows and attending; then the same step
+    through nvfp4_decode_step_dev_len with the lengths in device memory (bound = length).
+    Returns (pool, g, out_step, out_dev_len)."""
+    dev = "cuda"
+    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev)
+    kd, vd = ref.k.to(dev), ref.v.to(dev)
+    lens = list(w.seq_lens)
+    g = qk.calibrate(pool, kd, vd, lens)
+    zero = [0] * w.batch
+    pre = [L - w.n_q for L in lens]
+    if w.append_rows:
+        L0 = w.capacity - w.append_rows
+        qk.append(pool, kd[:L0].contiguous(), vd[:L0].contiguous(), g, [0], [0], [L0])
+        qk.append(pool, kd[L0:pre[0]].contiguous(), vd[L0:pre[0]].contiguous(), g, [0], [L0], [pre[0] - L0])
+    else:
+        qk.append(pool, _seq_rows(kd, w, zero, pre), _seq_rows(vd, w, zero, pre), g, w.seq_base, zero, pre)
+    k_step, v_step = _seq_rows(kd, w, pre, lens), _seq_rows(vd, w, pre, lens)
+    del kd, vd
+    q = ref.q.to(dev)
+    ws = qk.alloc_workspace(pool, lens, w.n_q, w.num_q_heads)
+    out = qk.decode_step(pool, g, k_step, v_step, q, w.seq_base, lens, w.sm_scale, workspace=ws)
+    out_dl = None
+    if w.rows <= 128:
+        lens_dev = torch.tensor(lens, dtype=torch.int64, device=dev)
+        out_dl = qk.decode_step_dev_len(pool, g, k_step, v_step, q, w.seq_base, lens, lens_dev, w.sm_scale,
+                                        workspace=ws)
+    torch.cuda.synchronize()
+    return pool, g, out, out_dl
+
+
+def _prefill_rows(w):
+    return [(b, i, h) for b in range(w.batch) for i in (0, 1, w.n_q // 2, w.n_q - 1) for h in range(w.num_q_heads)]
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,per_head", [("tiny", None), ("decode_27b", None), ("mtp_verify", 3),
-                                           ("long_agentic", 1), ("dflash_verify", 3)])
-def test_full_workload(qk, name, per_head):
+@pytest.mark.parametrize("name", ["tiny", "decode_27b", "mtp_verify", "long_agentic", "append_max_context",
+                                  "dflash_verify", "prefill_chunk"])
+def test_full_workload_step(qk, name):
+    """Every configuration at full size through the timed decode step: the pool bytes (the
+    step's own rows included) bit-exact against the oracle's, and every query row's output
+    within tolerance (prefill_chunk, 24,576 rows: every head of four query tokens)."""
     w = workloads.get(name)
-    say("full workload", name, w.seq_lens)
+    say("full workload", name, w.seq_lens, "n_q", w.n_q)
     ref = OracleRun(w)
-    say("  oracle quantised; running GPU")
-    pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
+    say("  oracle quantised; running the GPU step")
+    pool, g, out, out_dl = _full_step(qk, w, ref)
     assert np.array_equal(g.cpu().numpy(), ref.g)
     assert_planes_equal(pool, ref.cache)
     say("  planes bit-exact; oracle attention")
-    sel = None if per_head is None else _sample_rows(w, per_head)
-    if name == "long_agentic":
-        sel = sel[::3]
+    sel = _prefill_rows(w) if name == "prefill_chunk" else None
     _check_decode(w, ref, out, sel=sel)
+    if out_dl is not None:
+        say("  device-length step")
+        _check_decode(w, ref, out_dl, sel=sel)
 
 
-@pytest.mark.timeout(900)
-def test_full_append_max_context(qk):
-    """600000-token cache: the first 591808 rows appended, then the timed 8192-row
-    prefill chunk at positions 591808..599999, then decode over all 600000."""
-    w = workloads.get("append_max_context")
-    say("full workload append_max_context")
-    ref = OracleRun(w)
-    import quantized_kv_decode_amd as qk_
-    dev = "cuda"
-    pool = qk_.KVPool(w.num_kv_heads, w.head_dim, w.capacity)
-    kd, vd = ref.k.to(dev), ref.v.to(dev)
-    g = qk_.calibrate(pool, kd, vd, [w.capacity])
-    L0 = w.capacity - w.append_rows
-    qk_.append(pool, kd[:L0].contiguous(), vd[:L0].contiguous(), g, [0], [0], [L0])
-    qk_.append(pool, kd[L0:].contiguous(), vd[L0:].contiguous(), g, [0], [L0], [w.append_rows])
-    del kd, vd
-    out = qk_.decode_attn(pool, g, ref.q.to(dev), [0], [w.capacity], w.sm_scale)
+@pytest.mark.parametrize("nbytes,wg", [(64 * 1024 * 1024 + 48, 1024), ((1 << 31) + (1 << 24) + 16, 4096)])
+def test_read_probe_reads_every_word_once(qk, nbytes, wg):
+    """The streaming-read probe folds every 32-bit word of the buffer exactly once (the XOR of
+    its per-workgroup checksums equals the XOR of the buffer), including a ragged tail and a
+    buffer past the 2 GiB window of one raw buffer descriptor."""
+    say("read probe", nbytes, "bytes,", wg, "workgroups")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=gen)
+    sink = qk.hbm_read_probe(buf, wg)
     torch.cuda.synchronize()
-    assert_planes_equal(pool, ref.cache)
-    _check_decode(w, ref, out)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    exp = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
+    assert got == exp
+    del buf
