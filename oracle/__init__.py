@@ -23,6 +23,9 @@ Pins (tests run with ``-m "not gpu"``):
   * dequantize_rows: the quantiser's error bound against the original inputs.
   * attention: torch float64 scaled_dot_product_attention on the dequantised
     tensors, brute-force invariants and the causal reduction.
+  * quantize_rows_fp8 / dequantize_rows_fp8 (the K half of K8V4, row-scaled FP8
+    E4M3): hand-worked rows under tests/golden, exact-rational brute force of the
+    row scale and every code, error-bound and re-encoding invariants.
 """
 from __future__ import annotations
 
@@ -73,7 +76,11 @@ def _load():
         lib.orc_quantize_rows.restype = None
         lib.orc_dequantize_rows.argtypes = [vp, vp, c_i64, c_i32, vp, vp]
         lib.orc_dequantize_rows.restype = None
-        lib.orc_attention.argtypes = [vp, vp, vp, vp, c_i32, c_i32, c_i64, vp, vp, c_i32, vp, vp,
+        lib.orc_quantize_rows_fp8.argtypes = [vp, c_i64, c_i32, vp, vp, ctypes.c_int]
+        lib.orc_quantize_rows_fp8.restype = None
+        lib.orc_dequantize_rows_fp8.argtypes = [vp, vp, c_i64, c_i32, vp]
+        lib.orc_dequantize_rows_fp8.restype = None
+        lib.orc_attention.argtypes = [vp, vp, vp, vp, c_i32, c_i32, c_i32, c_i64, vp, vp, c_i32, vp, vp,
                                       c_i32, c_i32, c_dbl, c_i64, vp, vp, ctypes.c_int]
         lib.orc_attention.restype = ctypes.c_int
         _lib = lib
@@ -158,21 +165,58 @@ def dequantize_rows(codes: np.ndarray, scales: np.ndarray, g) -> np.ndarray:
     return out
 
 
-class Cache:
-    """Host copy of the packed KV pool: planes [Hkv][capacity][D/2] and [Hkv][capacity][D/16]."""
+def quantize_rows_fp8(x_u16: np.ndarray, nthreads: int | None = None):
+    """Row-scaled FP8 E4M3 (the K half of K8V4) of rows [..., D] of bf16 bit patterns.
 
-    def __init__(self, num_kv_heads: int, head_dim: int, capacity: int):
-        self.Hkv, self.D, self.capacity = num_kv_heads, head_dim, capacity
-        self.k_codes = np.zeros((num_kv_heads, capacity, head_dim // 2), dtype=np.uint8)
-        self.k_scales = np.zeros((num_kv_heads, capacity, head_dim // 16), dtype=np.uint8)
-        self.v_codes = np.zeros_like(self.k_codes)
-        self.v_scales = np.zeros_like(self.k_scales)
+    Returns (codes uint8 [..., D], scales float32 [...]): s = fp32(amax_row / 448), code =
+    sign << 7 | nearest E4M3 magnitude code of |x| / s (ties to even, saturating at 448).
+    """
+    x = np.ascontiguousarray(x_u16, dtype=np.uint16)
+    D = x.shape[-1]
+    n = x.size // D
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    _load().orc_quantize_rows_fp8(_ptr(x), n, D, _ptr(codes), _ptr(scales), nthreads or default_threads())
+    return codes, scales
+
+
+def dequantize_rows_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.float32)
+    D = c.shape[-1]
+    out = np.empty(c.shape, dtype=np.float64)
+    _load().orc_dequantize_rows_fp8(_ptr(c), _ptr(s), c.size // D, D, _ptr(out))
+    return out
+
+
+KV_FORMATS = ("nvfp4", "k8v4")
+
+
+class Cache:
+    """Host copy of the packed KV pool.
+
+    nvfp4: K and V planes [Hkv][capacity][D/2] codes and [Hkv][capacity][D/16] E4M3 scales.
+    k8v4:  V as above; K codes [Hkv][capacity][D] (E4M3) and fp32 row scales [Hkv][capacity].
+    """
+
+    def __init__(self, num_kv_heads: int, head_dim: int, capacity: int, kv_format: str = "nvfp4"):
+        assert kv_format in KV_FORMATS
+        self.Hkv, self.D, self.capacity, self.kv_format = num_kv_heads, head_dim, capacity, kv_format
+        self.v_codes = np.zeros((num_kv_heads, capacity, head_dim // 2), dtype=np.uint8)
+        self.v_scales = np.zeros((num_kv_heads, capacity, head_dim // 16), dtype=np.uint8)
+        if kv_format == "k8v4":
+            self.k_codes = np.zeros((num_kv_heads, capacity, head_dim), dtype=np.uint8)
+            self.k_scales = np.zeros((num_kv_heads, capacity), dtype=np.float32)
+        else:
+            self.k_codes = np.zeros_like(self.v_codes)
+            self.k_scales = np.zeros_like(self.v_scales)
 
 
 def append(cache: Cache, k_new: np.ndarray, v_new: np.ndarray, g: np.ndarray, seq_base, write_pos,
            n_new, nthreads: int | None = None) -> None:
     """Quantise n_new[b] rows per sequence (bf16 [sum n_new][Hkv][D], concatenated over b)
-    into slots seq_base[b] + write_pos[b] + r of every head plane, with g[b][h][0|1]."""
+    into slots seq_base[b] + write_pos[b] + r of every head plane, with g[b][h][0|1] (K8V4:
+    K rows row-scaled FP8, g[b][h][0] unused)."""
     r0 = 0
     for b, n in enumerate(n_new):
         if n == 0:
@@ -180,7 +224,10 @@ def append(cache: Cache, k_new: np.ndarray, v_new: np.ndarray, g: np.ndarray, se
         s0 = seq_base[b] + write_pos[b]
         assert s0 + n <= cache.capacity
         for h in range(cache.Hkv):
-            kc, ks = quantize_rows(k_new[r0:r0 + n, h], g[b, h, 0], nthreads)
+            if cache.kv_format == "k8v4":
+                kc, ks = quantize_rows_fp8(k_new[r0:r0 + n, h], nthreads)
+            else:
+                kc, ks = quantize_rows(k_new[r0:r0 + n, h], g[b, h, 0], nthreads)
             vc, vs = quantize_rows(v_new[r0:r0 + n, h], g[b, h, 1], nthreads)
             cache.k_codes[h, s0:s0 + n] = kc
             cache.k_scales[h, s0:s0 + n] = ks
@@ -208,7 +255,8 @@ def attention(cache: Cache, g: np.ndarray, q_u16: np.ndarray, seq_base, seq_len,
     base = np.ascontiguousarray(seq_base, dtype=np.int64)
     lens = np.ascontiguousarray(seq_len, dtype=np.int64)
     rc = _load().orc_attention(_ptr(cache.k_codes), _ptr(cache.k_scales), _ptr(cache.v_codes),
-                               _ptr(cache.v_scales), cache.Hkv, D, cache.capacity, _ptr(gs), _ptr(q), B,
+                               _ptr(cache.v_scales), 1 if cache.kv_format == "k8v4" else 0, cache.Hkv, D,
+                               cache.capacity, _ptr(gs), _ptr(q), B,
                                _ptr(base), _ptr(lens), n_q, Hq, float(sm_scale), sel_a.shape[0],
                                _ptr(sel_a), _ptr(out), nthreads or default_threads())
     if rc != 0:

@@ -23,6 +23,14 @@
  *     query token i of n_q seeing keys [0, L - n_q + i] (the n_q query tokens' own
  *     K/V are the last n_q rows of the context).
  *
+ * K8V4 (knoopx/ninfer page, "Capabilities and limits", KV storage list: 8-bit K with 4-bit
+ * V) is stored with K as row-scaled FP8 E4M3 (the 8-bit K format is not given there; this
+ * reading takes the engine's row-scaled FP8 E4M3 storage, knoopx/ninfer page, "Performance":
+ * "FP8 E4M3 row-256", one scale per 256-element row, and gzenz/ninfer page, "Capabilities and
+ * limits"): per (token, KV head) row, s = fp32(amax_row / 448) and each element's code is the
+ * E4M3 value nearest the exact real x / s (ties to the even code, saturating at 448, sign bit
+ * copied); x_hat = e4m3(code) * s. V is NVFP4 as above.
+ *
  * Exactness of the rounding decisions. Every comparison below is of the form
  * a (vs) t * b with a exact and t * b an exact fp64 product:
  *   - scale:   a = amax (a bf16 value), b = 6 g (g has 24 significant bits, so 6 g
@@ -158,6 +166,26 @@ static void quantize_row(const uint16_t *x, int32_t D, float g, uint8_t *codes, 
     }
 }
 
+/* Row-scaled FP8 E4M3 (the K half of K8V4): s = fp32(amax / 448) over the row's D bf16
+ * values (the fp64 quotient rounded once to fp32 is the correctly rounded fp32 quotient);
+ * code d = sign(x_d) << 7 | the E4M3 magnitude code nearest |x_d| / s (exact: a midpoint
+ * times s has at most 5 + 24 significant bits). s = 0 gives magnitude 0. */
+static void quantize_row_fp8(const uint16_t *x, int32_t D, uint8_t *codes, float *scale)
+{
+    double amax = 0.0;
+    for (int32_t d = 0; d < D; ++d) {
+        double v = fabs(bf16_value(x[d]));
+        if (v > amax) amax = v;
+    }
+    float s = (float)(amax / 448.0);
+    *scale = s;
+    for (int32_t d = 0; d < D; ++d) {
+        int sign = (x[d] >> 15) & 1;
+        int mag = orc_e4m3_encode(fabs(bf16_value(x[d])), (double)s);
+        codes[d] = (uint8_t)((sign << 7) | mag);
+    }
+}
+
 /* ----------------------------------------------------------- thread helper */
 
 typedef void (*work_fn)(void *ctx, int64_t item);
@@ -209,6 +237,33 @@ void orc_quantize_rows(const uint16_t *x, int64_t n_rows, int32_t D, const float
     parallel_for(quant_item, &c, n_rows, nthreads);
 }
 
+typedef struct {
+    const uint16_t *x; int32_t D; uint8_t *codes; float *scales;
+} quant8_ctx;
+
+static void quant8_item(void *p, int64_t r)
+{
+    quant8_ctx *c = (quant8_ctx *)p;
+    quantize_row_fp8(c->x + r * c->D, c->D, c->codes + r * c->D, c->scales + r);
+}
+
+/* Row-scaled FP8 E4M3: n_rows rows of D bf16 values -> D code bytes and one fp32 scale each. */
+void orc_quantize_rows_fp8(const uint16_t *x, int64_t n_rows, int32_t D, uint8_t *codes, float *scales,
+                           int nthreads)
+{
+    tables();
+    quant8_ctx c = {x, D, codes, scales};
+    parallel_for(quant8_item, &c, n_rows, nthreads);
+}
+
+/* x_hat = e4m3(code) * s, one row of D values per r. */
+void orc_dequantize_rows_fp8(const uint8_t *codes, const float *scales, int64_t n_rows, int32_t D, double *out)
+{
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int32_t d = 0; d < D; ++d)
+            out[r * D + d] = orc_e4m3_value(codes[r * D + d]) * (double)scales[r];
+}
+
 /* x_hat = e2m1(code) * e4m3(scale) * g, one row of D values per r. */
 void orc_dequantize_rows(const uint8_t *codes, const uint8_t *scales, int64_t n_rows, int32_t D,
                          const float *g, double *out)
@@ -226,6 +281,7 @@ void orc_dequantize_rows(const uint8_t *codes, const uint8_t *scales, int64_t n_
 
 typedef struct {
     const uint8_t *kc, *ks, *vc, *vs;
+    int32_t k_fp8;                 /* 0: K is NVFP4; 1: K is row-scaled FP8 E4M3 (K8V4) */
     int32_t Hkv, D; int64_t cap;
     const float *gscale;
     const uint16_t *q;
@@ -243,6 +299,12 @@ static double khat(const uint8_t *codes, const uint8_t *scales, int32_t D, int64
     return E2M1_ALL[code] * E4M3_ALL[scales[slot * (D / 16) + d / 16]] * g;
 }
 
+/* Element d of token slot t of a row-scaled FP8 head plane (codes [cap][D], scales [cap]). */
+static double khat_fp8(const uint8_t *codes, const float *scales, int32_t D, int64_t slot, int32_t d)
+{
+    return E4M3_ALL[codes[slot * D + d]] * (double)scales[slot];
+}
+
 static void attn_item(void *p, int64_t n)
 {
     attn_ctx *c = (attn_ctx *)p;
@@ -253,7 +315,8 @@ static void attn_item(void *p, int64_t n)
     double gk = c->gscale[(b * c->Hkv + kh) * 2 + 0];
     double gv = c->gscale[(b * c->Hkv + kh) * 2 + 1];
     const uint16_t *qrow = c->q + (((int64_t)b * c->n_q + i) * c->Hq + h) * D;
-    const uint8_t *kc = c->kc + (int64_t)kh * c->cap * (D / 2), *ks = c->ks + (int64_t)kh * c->cap * (D / 16);
+    const uint8_t *kc = c->k_fp8 ? c->kc + (int64_t)kh * c->cap * D : c->kc + (int64_t)kh * c->cap * (D / 2);
+    const uint8_t *ks = c->k_fp8 ? c->ks + (int64_t)kh * c->cap * 4 : c->ks + (int64_t)kh * c->cap * (D / 16);
     const uint8_t *vc = c->vc + (int64_t)kh * c->cap * (D / 2), *vs = c->vs + (int64_t)kh * c->cap * (D / 16);
     double *o = c->out + n * D;
     double *qd = (double *)malloc(sizeof(double) * D);
@@ -265,7 +328,10 @@ static void attn_item(void *p, int64_t n)
     double m = -INFINITY;
     for (int64_t t = 0; t < nvis; ++t) {
         double acc = 0.0;
-        for (int32_t d = 0; d < D; ++d) acc += qd[d] * khat(kc, ks, D, base + t, d, gk);
+        if (c->k_fp8)
+            for (int32_t d = 0; d < D; ++d) acc += qd[d] * khat_fp8(kc, (const float *)ks, D, base + t, d);
+        else
+            for (int32_t d = 0; d < D; ++d) acc += qd[d] * khat(kc, ks, D, base + t, d, gk);
         s[t] = c->sm_scale * acc;
         if (s[t] > m) m = s[t];
     }
@@ -281,11 +347,13 @@ static void attn_item(void *p, int64_t n)
 }
 
 /* Decode attention for the selected (b, i, h) triples sel[3n..3n+2]; out[n][D].
- * Planes are [Hkv][capacity][D/2] codes and [Hkv][capacity][D/16] scales;
+ * V planes are [Hkv][capacity][D/2] codes and [Hkv][capacity][D/16] scales; so are the K
+ * planes when k_fp8 = 0, while k_fp8 = 1 (K8V4) takes K codes [Hkv][capacity][D] (E4M3) and
+ * fp32 row scales [Hkv][capacity];
  * gscale is [B][Hkv][2] (0 = K, 1 = V); q is bf16 [B][n_q][Hq][D].
  * Returns 0, or -1 on bad arguments / allocation failure. */
 int orc_attention(const uint8_t *k_codes, const uint8_t *k_scales, const uint8_t *v_codes,
-                  const uint8_t *v_scales, int32_t Hkv, int32_t D, int64_t capacity,
+                  const uint8_t *v_scales, int32_t k_fp8, int32_t Hkv, int32_t D, int64_t capacity,
                   const float *gscale, const uint16_t *q, int32_t B, const int64_t *seq_base,
                   const int64_t *seq_len, int32_t n_q, int32_t Hq, double sm_scale, int64_t n_sel,
                   const int32_t *sel, double *out, int nthreads)
@@ -297,7 +365,7 @@ int orc_attention(const uint8_t *k_codes, const uint8_t *k_scales, const uint8_t
         if (b < 0 || b >= B || i < 0 || i >= n_q || h < 0 || h >= Hq) return -1;
         if (seq_len[b] < n_q || seq_base[b] < 0 || seq_base[b] + seq_len[b] > capacity) return -1;
     }
-    attn_ctx c = {k_codes, k_scales, v_codes, v_scales, Hkv, D, capacity, gscale, q,
+    attn_ctx c = {k_codes, k_scales, v_codes, v_scales, k_fp8 != 0, Hkv, D, capacity, gscale, q,
                   seq_base, seq_len, n_q, Hq, sm_scale, sel, out, 0};
     parallel_for(attn_item, &c, n_sel, nthreads);
     return c.status;

@@ -29,10 +29,14 @@ import torch
 
 CHUNK_ROWS = 4096
 
-# Bytes per token per KV head of the packed layout: K and V each carry D/2
-# code bytes (two E2M1 codes per byte) and D/16 E4M3 scale bytes.
-def packed_bytes_per_token_head(head_dim: int) -> int:
-    return 2 * (head_dim // 2 + head_dim // 16)
+# Bytes per token per KV head of the packed layout. NVFP4: K and V each carry D/2 code
+# bytes (two E2M1 codes per byte) and D/16 E4M3 scale bytes. K8V4: K carries D E4M3 code
+# bytes and one fp32 row scale, V is NVFP4.
+def packed_bytes_per_token_head(head_dim: int, kv_format: str = "nvfp4") -> int:
+    v = head_dim // 2 + head_dim // 16
+    if kv_format == "k8v4":
+        return head_dim + 4 + v
+    return 2 * v
 
 
 @dataclass(frozen=True)
@@ -49,6 +53,7 @@ class Workload:
     outlier_gain: float = 20.0
     append_rows: int = 0          # size of the separately timed prefill-chunk append (0: none)
     description: str = ""
+    kv_format: str = "nvfp4"      # "nvfp4", or "k8v4" (row-scaled FP8 E4M3 K, NVFP4 V)
 
     # ---- derived shapes -------------------------------------------------
     @property
@@ -89,7 +94,7 @@ class Workload:
     @property
     def kv_bytes(self) -> int:
         """Packed K+V bytes one decode step must read (codes + E4M3 scales)."""
-        return self.capacity * self.num_kv_heads * packed_bytes_per_token_head(self.head_dim)
+        return self.capacity * self.num_kv_heads * packed_bytes_per_token_head(self.head_dim, self.kv_format)
 
     @property
     def visible_keys(self) -> int:
@@ -135,6 +140,17 @@ WORKLOADS = {
 }
 
 ORDER = ["tiny", "decode_27b", "mtp_verify", "long_agentic", "append_max_context"]
+
+# The same five configurations stored as K8V4 (8-bit K, NVFP4 V): same seeds, so the same
+# bf16 inputs as their NVFP4 versions.
+for _n in ORDER:
+    _w = WORKLOADS[_n]
+    WORKLOADS[_n + "_k8v4"] = Workload(
+        _n + "_k8v4", _w.index, _w.seq_lens, _w.num_kv_heads, _w.num_q_heads, _w.head_dim, _w.n_q,
+        v_dist=_w.v_dist, outlier_frac=_w.outlier_frac, outlier_gain=_w.outlier_gain,
+        append_rows=_w.append_rows, description=_w.description + "; K8V4 (row-scaled FP8 K, NVFP4 V)",
+        kv_format="k8v4")
+ORDER_K8V4 = [n + "_k8v4" for n in ORDER]
 
 
 def get(name: str) -> Workload:
@@ -226,7 +242,7 @@ def from_u16(a: np.ndarray) -> torch.Tensor:
 
 
 def small(name: str = "small", seq_lens=(200, 77), num_kv_heads=2, num_q_heads=6, head_dim=256,
-          n_q=3, v_dist="normal", outlier_frac=0.0, index=9) -> Workload:
+          n_q=3, v_dist="normal", outlier_frac=0.0, index=9, kv_format="nvfp4") -> Workload:
     """Ad-hoc workload for parity tests: several tiles, a ragged tail, same generators."""
     return Workload(name, index, tuple(seq_lens), num_kv_heads, num_q_heads, head_dim, n_q,
-                    v_dist=v_dist, outlier_frac=outlier_frac)
+                    v_dist=v_dist, outlier_frac=outlier_frac, kv_format=kv_format)
