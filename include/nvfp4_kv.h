@@ -185,6 +185,26 @@ int nvfp4_decode_step_dev_len(const nvfp4_kv_cache *cache, const float *global_s
                               const int64_t *seq_len_dev, int32_t n_q, int32_t num_q_heads,
                               float sm_scale, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Capacity of the static scratch array that nvfp4_decode_step_noalloc uses (MiB). */
+#define NVFP4_NOALLOC_SCRATCH_MIB 32
+
+/* nvfp4_decode_step for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same arguments, results
+ * and errors as nvfp4_decode_step, without the workspace: the split-K partials go to a
+ * fixed device array inside the library (NVFP4_NOALLOC_SCRATCH_MIB MiB per GPU, held until
+ * the process ends). The call allocates nothing; its first call on a device looks the
+ * array's address up (hipGetSymbolAddress).
+ *   - A step whose partials need more than the array holds (the size query
+ *     nvfp4_decode_attn_workspace_bytes says how many bytes) is rejected with
+ *     NVFP4_EWORKSPACE before any launch; nvfp4_decode_step with a caller workspace serves it.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap in time (on
+ *     different streams) race and give wrong results. Calls on one stream are ordered.
+ *   - NVFP4_EHIP also if the device or the array's address cannot be queried. */
+int nvfp4_decode_step_noalloc(const nvfp4_kv_cache *cache, const float *global_scale, const void *k_new,
+                              const void *v_new, const void *q, void *out, int32_t out_dtype,
+                              int32_t num_seqs, const int64_t *seq_base, const int64_t *seq_len,
+                              int32_t n_q, int32_t num_q_heads, float sm_scale, void *stream);
+
 /* The two kernels of nvfp4_decode_attn, callable on their own (same arguments,
  * same workspace) so that each can be timed: the split-K partial pass writes
  * per-split (o, m, l) into the workspace; the combine pass merges them by

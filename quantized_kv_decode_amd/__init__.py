@@ -29,7 +29,7 @@ _ERR_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ERANGE: "ERANGE",
               EWORKSPACE: "EWORKSPACE", EHIP: "EHIP"}
 
 SYMBOLS = ["nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn_workspace_bytes",
-           "nvfp4_decode_attn", "nvfp4_decode_step", "nvfp4_decode_step_dev_len",
+           "nvfp4_decode_attn", "nvfp4_decode_step", "nvfp4_decode_step_dev_len", "nvfp4_decode_step_noalloc",
            "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine", "nvfp4_hbm_read_probe",
            "nvfp4_last_error"]
 
@@ -71,11 +71,12 @@ def load_library():
     lib.nvfp4_decode_attn_partial.argtypes = [P, vp, vp, i32, i64, i64, i32, i32, f32, vp, sz, vp]
     lib.nvfp4_decode_attn_combine.argtypes = [P, vp, vp, i32, i32, i64, i32, i32, vp, sz, vp]
     lib.nvfp4_hbm_read_probe.argtypes = [vp, sz, vp, i32, vp]
+    lib.nvfp4_decode_step_noalloc.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, i64, i64, i32, i32, f32, vp]
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_last_error.restype = ctypes.c_char_p
     for f in ("nvfp4_kv_calibrate", "nvfp4_kv_append", "nvfp4_decode_attn", "nvfp4_decode_step",
               "nvfp4_decode_step_dev_len", "nvfp4_decode_attn_partial", "nvfp4_decode_attn_combine",
-              "nvfp4_hbm_read_probe"):
+              "nvfp4_hbm_read_probe", "nvfp4_decode_step_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -194,6 +195,20 @@ def decode_step(pool: KVPool, global_scale: torch.Tensor, k_new: torch.Tensor, v
     _check(load_library().nvfp4_decode_step(ctypes.byref(d), _ptr(global_scale), _ptr(k_new), _ptr(v_new), _ptr(q),
                                             _ptr(out), code, B, _i64(seq_base), _i64(seq_len), n_q, Hq,
                                             float(sm_scale), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_step_noalloc(pool: KVPool, global_scale: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        q: torch.Tensor, seq_base, seq_len, sm_scale: float, out: torch.Tensor,
+                        stream=None) -> torch.Tensor:
+    """decode_step without a workspace: the partials go to the library's static per-GPU scratch
+    array (nothing is allocated; `out` must be given). Calls that overlap on one GPU race."""
+    B, n_q, Hq, D = q.shape
+    code = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    d = pool.desc()
+    _check(load_library().nvfp4_decode_step_noalloc(ctypes.byref(d), _ptr(global_scale), _ptr(k_new), _ptr(v_new),
+                                                    _ptr(q), _ptr(out), code, B, _i64(seq_base), _i64(seq_len), n_q,
+                                                    Hq, float(sm_scale), _stream(stream)))
     return out
 
 

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libnvfp4kv.so")
-SOURCES = ["api.cpp", "append.hip", "decode.hip", "decode_pair.hip", "probe.hip"]
+SOURCES = ["api.cpp", "append.hip", "decode.hip", "decode_pair.hip", "probe.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
