@@ -138,7 +138,7 @@ def hbm_probe(dev, nbytes: int = 1 << 30):
     sink = torch.empty(16384, dtype=torch.int32, device=dev)
     s = torch.cuda.current_stream()
     best, rates = 0.0, {}
-    for wg in (1024, 2048, 4096, 8192, 16384):
+    for wg in (256, 512, 768, 1024, 1536, 2048, 4096, 8192):
         for _ in range(3):
             qk.hbm_read_probe(buf, wg, sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
