@@ -88,7 +88,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
         ku = np.ascontiguousarray(k_rows[:, kh:kh + 1])
         vu = np.ascontiguousarray(v_rows[:, kh:kh + 1])
         g = oracle.calibrate(ku, vu, [L])
-        cache = oracle.Cache(1, w.head_dim, L)
+        cache = oracle.Cache(1, w.head_dim, L, kv_format=w.kv_format)
         oracle.append(cache, ku, vu, g, [0], [0], [L - w.n_q], nthreads)
         q = np.ascontiguousarray(q_all[b:b + 1, :, kh * w.group:(kh + 1) * w.group])
         kn, vn = np.ascontiguousarray(ku[L - w.n_q:]), np.ascontiguousarray(vu[L - w.n_q:])
@@ -107,7 +107,8 @@ def cpu_baseline(w, budget_s: float = 12.0):
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 1000:
             break
-    bytes_per_step = len(heads) * L * workloads.packed_bytes_per_token_head(w.head_dim)
+    bytes_per_token = workloads.packed_bytes_per_token_head(w.head_dim, w.kv_format)
+    bytes_per_step = len(heads) * L * bytes_per_token
     # one thread: the G rows of the first query token of the first sampled head
     t1 = time.perf_counter()
     step(*parts[0], 1, sel=[(0, 0, h) for h in range(w.group)])
@@ -124,8 +125,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "ms_per_step": round(el / steps * 1e3, 3), "threads": nthreads, "nproc": os.cpu_count(),
             "affinity_cpus": affinity,
             "single_thread": {"rows": w.group, "keys_per_row": L - w.n_q + 1, "ms": round(el1 * 1e3, 3),
-                              "GBps": round(L * workloads.packed_bytes_per_token_head(w.head_dim) / el1 / 1e9
-                                            * w.group / (w.group * w.n_q), 4)},
+                              "GBps": round(L * bytes_per_token / el1 / 1e9 * w.group / (w.group * w.n_q), 4)},
             "cpu_model": cpu_model()}
 
 
@@ -193,7 +193,7 @@ def main() -> int:
 
     # ---- resident inputs: one calibrated, filled pool, then rotation copies
     log(f"workload {w.name}: {w.description}")
-    pool0 = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev)
+    pool0 = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev, kv_format=w.kv_format)
     g = torch.empty((w.batch, w.num_kv_heads, 2), dtype=torch.float32, device=dev)
     kdev, vdev = [], []
     for b in range(w.batch):                                   # upload per sequence
@@ -389,7 +389,9 @@ def main() -> int:
             "num_q_heads": w.num_q_heads,
             "head_dim": w.head_dim,
             "n_q": w.n_q,
-            "kv_format": "nvfp4 (e2m1 codes + e4m3 group-16 scales + fp32 per-(seq, kv head) scale)",
+            "kv_format": ("nvfp4 (e2m1 codes + e4m3 group-16 scales + fp32 per-(seq, kv head) scale)"
+                          if w.kv_format == "nvfp4" else
+                          "k8v4 (K: e4m3 codes + fp32 row scale; V: nvfp4 as above)"),
             "kv_bytes_per_step": kv,
             "rotation_copies": R,
             "timing": "one HIP-graph replay of K steps between events",

@@ -23,10 +23,21 @@
  *                      g = fp32(amax / (6*448)) over that sequence's rows of that
  *                      head (second-level scale; not on the pages, a stated reading).
  * Element value: x_hat = e2m1(code) * e4m3(scale) * g.
+ * K8V4 pools (kv_format = NVFP4_KV_K8V4: 8-bit K with 4-bit V, knoopx/ninfer page,
+ * "Capabilities and limits", KV storage list) keep V as above and store K row-scaled in
+ * FP8 E4M3, the engine's 8-bit KV format (knoopx/ninfer page, "Performance": FP8 E4M3
+ * row-256; the pages do not say which 8-bit format K8V4's K uses, so this is a reading):
+ *   k_codes   uint8 [num_kv_heads][capacity][head_dim], byte d = E4M3FN code of element d
+ *             (sign << 7 | magnitude code 0x00..0x7E)
+ *   k_scales  float [num_kv_heads][capacity], the row scale s = fp32(amax_row / 448)
+ *   K element value: e4m3(code) * s; global_scale[b][h][0] is not used for K.
+ *   Bytes per (token, KV head): head_dim + 4 for K, head_dim/2 + head_dim/16 for V.
  * Sequence b owns slots [seq_base[b], seq_base[b] + length) in every head plane.
  * Quantisation rounds the exact real ratios amax_group/(6g) and |x|/(S g) to the
  * nearest E4M3 / E2M1 value, ties to the even code, saturating at 448 / 6; the
  * input's sign bit becomes the code's sign bit; g == 0 gives scale 0 and zero
+ * magnitudes. K8V4's K rows: each element's code is the E4M3 value nearest the exact real
+ * |x| / s, ties to the even code, saturating at 448, sign bit copied; s == 0 gives zero
  * magnitudes.
  *
  * ------------------------------------------------------------ conventions ---
@@ -62,13 +73,17 @@ extern "C" {
 #define NVFP4_OUT_F32  0
 #define NVFP4_OUT_BF16 1
 
+#define NVFP4_KV_NVFP4 0         /* kv_format: K and V both NVFP4                      */
+#define NVFP4_KV_K8V4  1         /* kv_format: row-scaled FP8 E4M3 K, NVFP4 V          */
+
 #define NVFP4_MAX_SEQS 8         /* active sequences per call                         */
 #define NVFP4_MAX_ROWS 8192      /* GQA group x query tokens sharing one KV head      */
 
 /* The caller-owned pool. head_dim must be 128 or 256; num_kv_heads >= 1;
- * capacity >= 1 token slots per head plane, and capacity * head_dim / 2 (one
- * head's code plane in bytes) at most 2^31 - 1, since kernels address a head
- * plane with 32-bit offsets (else NVFP4_EUNSUPPORTED). */
+ * capacity >= 1 token slots per head plane, and one head's largest code plane in bytes
+ * (capacity * head_dim / 2; capacity * head_dim for K8V4's K) at most 2^31 - 1, since
+ * kernels address a head plane with 32-bit offsets (else NVFP4_EUNSUPPORTED).
+ * kv_format: NVFP4_KV_NVFP4 or NVFP4_KV_K8V4 (else NVFP4_EINVAL). */
 typedef struct nvfp4_kv_cache {
     void   *k_codes;
     void   *k_scales;
@@ -77,6 +92,7 @@ typedef struct nvfp4_kv_cache {
     int32_t num_kv_heads;
     int32_t head_dim;
     int64_t capacity;
+    int32_t kv_format;
 } nvfp4_kv_cache;
 
 /* Global scales from the rows that will be stored (second-level per-(sequence,
@@ -92,7 +108,10 @@ int nvfp4_kv_calibrate(const nvfp4_kv_cache *cache, const void *k_rows, const vo
                        int32_t num_seqs, const int64_t *n_rows, float *global_scale,
                        void *stream);
 
-/* Quantise-on-append: writes n_new[b] K and V rows of sequence b at slots
+/* Quantise-on-append (gzenz/ninfer page, "Context and model", NVFP4 KV cache bullet: K
+ * and V kept as E2M1 codes with E4M3 group-16 scales; knoopx/ninfer page, "Capabilities and
+ * limits": each request's rows go into the one shared, startup-fixed KV pool at its own
+ * slots): writes n_new[b] K and V rows of sequence b at slots
  * seq_base[b] + write_pos[b] + r (r < n_new[b]) of every head plane. Lengths are
  * the caller's to advance. Each 16-element group gets its E4M3 scale from its own
  * maximum and the given g; rows whose values exceed 2688 g saturate.
@@ -108,12 +127,18 @@ int nvfp4_kv_append(const nvfp4_kv_cache *cache, const void *k_new, const void *
 
 /* Bytes of device workspace nvfp4_decode_attn (and its two halves below) need
  * for these arguments; 0 if the arguments are invalid (the decode call then
- * reports why). The split-K plan depends only on the arguments. */
+ * reports why). The split-K plan depends only on the arguments. The caller owns and
+ * allocates the workspace, as it owns the pool (knoopx/ninfer page, "Capabilities and
+ * limits": the shared KV pool is sized at startup and stays fixed for the process lifetime,
+ * so a caller sizes this buffer once for its largest step). */
 size_t nvfp4_decode_attn_workspace_bytes(const nvfp4_kv_cache *cache, int32_t num_seqs,
                                          const int64_t *seq_len, int32_t n_q,
                                          int32_t num_q_heads);
 
-/* Grouped-query decode attention read directly from the NVFP4 pool.
+/* Grouped-query decode attention read directly from the NVFP4 pool (gzenz/ninfer page,
+ * "Context and model": attention over the NVFP4 KV cache; knoopx/ninfer page, "Capabilities
+ * and limits": one to eight active requests decoded as one batch, each with 1 + 1..5 MTP
+ * draft tokens verified together, hence n_q query tokens causal among themselves).
  *   q:        device bf16 [num_seqs][n_q][num_q_heads][head_dim]
  *   out:      device [num_seqs][n_q][num_q_heads][head_dim], fp32 or bf16 (out_dtype;
  *             bf16 is the round-to-nearest-even of the fp32 result)
@@ -205,10 +230,10 @@ int nvfp4_decode_step_noalloc(const nvfp4_kv_cache *cache, const float *global_s
                               int32_t num_seqs, const int64_t *seq_base, const int64_t *seq_len,
                               int32_t n_q, int32_t num_q_heads, float sm_scale, void *stream);
 
-/* The two kernels of nvfp4_decode_attn, callable on their own (same arguments,
- * same workspace) so that each can be timed: the split-K partial pass writes
- * per-split (o, m, l) into the workspace; the combine pass merges them by
- * log-sum-exp, applies the V global scale and writes out. */
+/* The two kernels of nvfp4_decode_attn (the same attention as nvfp4_decode_attn, whose
+ * passages they follow), callable on their own (same arguments, same workspace) so that each
+ * can be timed: the split-K partial pass writes per-split (o, m, l) into the workspace; the
+ * combine pass merges them by log-sum-exp, applies the V global scale and writes out. */
 int nvfp4_decode_attn_partial(const nvfp4_kv_cache *cache, const float *global_scale,
                               const void *q, int32_t num_seqs, const int64_t *seq_base,
                               const int64_t *seq_len, int32_t n_q, int32_t num_q_heads,

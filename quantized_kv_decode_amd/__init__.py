@@ -40,11 +40,15 @@ class Nvfp4Error(RuntimeError):
         self.code = code
 
 
+KV_NVFP4, KV_K8V4 = 0, 1
+KV_FORMATS = {"nvfp4": KV_NVFP4, "k8v4": KV_K8V4}
+
+
 class CacheDesc(ctypes.Structure):
     _fields_ = [("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
                 ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("capacity", ctypes.c_int64)]
+                ("capacity", ctypes.c_int64), ("kv_format", ctypes.c_int32)]
 
 
 _lib = None
@@ -104,21 +108,37 @@ def _ptr(t) -> int:
 
 
 class KVPool:
-    """Caller-owned NVFP4 pool: code and scale planes for K and V (torch uint8 tensors)."""
+    """Caller-owned pool: code and scale planes for K and V (torch tensors on the device).
 
-    def __init__(self, num_kv_heads: int, head_dim: int, capacity: int, device="cuda"):
+    nvfp4: every plane uint8, codes [Hkv][capacity][D/2], scales [Hkv][capacity][D/16].
+    k8v4:  V as above; K codes uint8 [Hkv][capacity][D] (E4M3), K row scales float32 [Hkv][capacity].
+    """
+
+    def __init__(self, num_kv_heads: int, head_dim: int, capacity: int, device="cuda", kv_format: str = "nvfp4"):
         self.num_kv_heads, self.head_dim, self.capacity = num_kv_heads, head_dim, capacity
+        self.kv_format = kv_format
         mk = lambda w: torch.zeros((num_kv_heads, capacity, w), dtype=torch.uint8, device=device)
-        self.k_codes, self.k_scales = mk(head_dim // 2), mk(head_dim // 16)
+        if kv_format == "k8v4":
+            self.k_codes = mk(head_dim)
+            self.k_scales = torch.zeros((num_kv_heads, capacity), dtype=torch.float32, device=device)
+        elif kv_format == "nvfp4":
+            self.k_codes, self.k_scales = mk(head_dim // 2), mk(head_dim // 16)
+        else:
+            raise ValueError(f"kv_format {kv_format!r}: 'nvfp4' or 'k8v4'")
         self.v_codes, self.v_scales = mk(head_dim // 2), mk(head_dim // 16)
 
     @classmethod
     def from_planes(cls, k_codes, k_scales, v_codes, v_scales):
         self = cls.__new__(cls)
-        self.num_kv_heads, self.capacity, half = k_codes.shape
+        self.num_kv_heads, self.capacity, half = v_codes.shape
         self.head_dim = 2 * half
+        self.kv_format = "k8v4" if k_scales.dim() == 2 else "nvfp4"
         self.k_codes, self.k_scales, self.v_codes, self.v_scales = k_codes, k_scales, v_codes, v_scales
         return self
+
+    def clone(self):
+        return KVPool.from_planes(self.k_codes.clone(), self.k_scales.clone(), self.v_codes.clone(),
+                                  self.v_scales.clone())
 
     @property
     def nbytes(self) -> int:
@@ -126,7 +146,8 @@ class KVPool:
 
     def desc(self) -> CacheDesc:
         return CacheDesc(self.k_codes.data_ptr(), self.k_scales.data_ptr(), self.v_codes.data_ptr(),
-                         self.v_scales.data_ptr(), self.num_kv_heads, self.head_dim, self.capacity)
+                         self.v_scales.data_ptr(), self.num_kv_heads, self.head_dim, self.capacity,
+                         KV_FORMATS[self.kv_format])
 
 
 def calibrate(pool: KVPool, k_rows: torch.Tensor, v_rows: torch.Tensor, n_rows, out: torch.Tensor | None = None,

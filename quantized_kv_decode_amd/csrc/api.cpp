@@ -46,10 +46,13 @@ int check_cache(const nvfp4_kv_cache *c) {
         return fail(NVFP4_EINVAL, "pool planes must be non-null and 16-byte aligned");
     if (c->num_kv_heads < 1) return fail(NVFP4_EINVAL, "num_kv_heads must be >= 1");
     if (c->capacity < 1) return fail(NVFP4_EINVAL, "capacity must be >= 1");
+    if (c->kv_format != NVFP4_KV_NVFP4 && c->kv_format != NVFP4_KV_K8V4)
+        return fail(NVFP4_EINVAL, "kv_format %d invalid (NVFP4_KV_NVFP4 or NVFP4_KV_K8V4)", c->kv_format);
     if (c->head_dim != 128 && c->head_dim != 256)
         return fail(NVFP4_EUNSUPPORTED, "head_dim %d unsupported (128 or 256)", c->head_dim);
-    // kernels address one head plane with 32-bit byte offsets
-    if (c->capacity > (int64_t)INT32_MAX / (c->head_dim / 2))
+    // kernels address one head plane with 32-bit byte offsets (K8V4's K codes: head_dim bytes a row)
+    const int64_t row_bytes = c->kv_format == NVFP4_KV_K8V4 ? c->head_dim : c->head_dim / 2;
+    if (c->capacity > (int64_t)INT32_MAX / row_bytes)
         return fail(NVFP4_EUNSUPPORTED, "capacity %lld too large: a head's code plane must stay below 2^31 bytes",
                     (long long)c->capacity);
     return NVFP4_OK;
@@ -169,6 +172,7 @@ void fill_decode(nvfp4::DecodeParams &dp, const nvfp4::SplitPlan &pl, const nvfp
     dp.vc = static_cast<uint8_t *>(c->v_codes);
     dp.vs = static_cast<uint8_t *>(c->v_scales);
     dp.cap = c->capacity;
+    dp.k_fp8 = c->kv_format == NVFP4_KV_K8V4;
     dp.gscale = global_scale;
     dp.q = static_cast<const uint16_t *>(q);
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -290,6 +294,7 @@ int nvfp4_kv_append(const nvfp4_kv_cache *cache, const void *k_new, const void *
     p.vc = static_cast<uint8_t *>(cache->v_codes);
     p.vs = static_cast<uint8_t *>(cache->v_scales);
     p.cap = cache->capacity;
+    p.k_fp8 = cache->kv_format == NVFP4_KV_K8V4;
     p.B = num_seqs;
     p.Hkv = cache->num_kv_heads;
     p.D = cache->head_dim;

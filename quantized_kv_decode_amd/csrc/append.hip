@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include "internal.h"
+#include "decode_common.h"
 #include "quantize.h"
 
 namespace nvfp4 {
@@ -14,8 +15,11 @@ using namespace dev;
 
 // One thread per (row, K|V, group of 16) of KV head blockIdx.y. Every divisor of the
 // index decomposition is a compile-time constant (head_dim is a template parameter;
-// divisions by run-time values cost tens of instructions each).
-template <int D>
+// divisions by run-time values cost tens of instructions each). A row's D/16 groups of K
+// (or of V) are D/16 consecutive threads, aligned, so K8V4's row-scaled FP8 K (KF = 1)
+// reduces its row maximum across them; every such run of threads is active as a whole
+// (the thread count is a multiple of D/16).
+template <int D, int KF>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     constexpr int groups = D / 16;
     const uint32_t tx = blockIdx.x * 256u + threadIdx.x;
@@ -35,9 +39,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const uint4 w1 = *reinterpret_cast<const uint4 *>(src + 8);
     const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 
+    const int64_t plane_row = (int64_t)h * p.cap + slot;
+    if (KF == 1 && kv == 0) {
+        store_fp8_group<D>(w, j, p.kc, p.ks, plane_row);
+        return;
+    }
     uint32_t packed[2];
     const uint32_t sc = quantize_group(w, p.gscale[(b * p.Hkv + h) * 2 + kv], packed);
-    const int64_t plane_row = (int64_t)h * p.cap + slot;
     uint8_t *codes = (kv ? p.vc : p.kc) + plane_row * (D / 2) + 8 * j;
     *reinterpret_cast<uint2 *>(codes) = make_uint2(packed[0], packed[1]);
     (kv ? p.vs : p.ks)[plane_row * groups + j] = (uint8_t)sc;
@@ -93,10 +101,14 @@ hipError_t launch_append(const AppendParams &p, hipStream_t s) {
     if (p.rows == 0) return hipSuccess;
     const int64_t threads = p.rows * 2 * (p.D / 16);  // per KV head; < 2^31 (checked by the caller)
     const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)p.Hkv);
-    if (p.D == 256)
-        hipLaunchKernelGGL(append_kernel<256>, grid, dim3(256), 0, s, p);
+    if (p.D == 256 && !p.k_fp8)
+        hipLaunchKernelGGL((append_kernel<256, 0>), grid, dim3(256), 0, s, p);
+    else if (p.D == 256)
+        hipLaunchKernelGGL((append_kernel<256, 1>), grid, dim3(256), 0, s, p);
+    else if (p.D == 128 && !p.k_fp8)
+        hipLaunchKernelGGL((append_kernel<128, 0>), grid, dim3(256), 0, s, p);
     else if (p.D == 128)
-        hipLaunchKernelGGL(append_kernel<128>, grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((append_kernel<128, 1>), grid, dim3(256), 0, s, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

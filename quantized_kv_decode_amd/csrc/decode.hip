@@ -52,48 +52,62 @@ namespace {
 
 using namespace dev;
 
-template <int D>
+// KF: the K format (0 NVFP4; 1 the row-scaled FP8 E4M3 K of K8V4), see KGeom.
+template <int D, int KF>
 struct Raw {
     static constexpr int EPL = D / 16;            // PV output tiles; d-values per token per lane
-    static constexpr int KW = D / 32;             // K code dwords per token per lane
+    static constexpr int KW = KF ? D / 16 : D / 32;   // K code dwords per token per lane
+    static constexpr int KS = KF ? 4 : 1;         // K scale dwords per tile per lane
     static constexpr int VW = EPL / 8;            // V code dwords per token per lane
     uint32_t k[2][KW];                            // two 16-token tiles
-    uint32_t ks[2];                               // K scale bytes (D/64 of them) per tile
+    uint32_t ks[2][KS];                           // NVFP4: the lane's D/64 scale bytes of token n;
+                                                  // FP8: fp32 row scales of tokens 16 mt + 4 g + i
     uint32_t v[8][VW];                            // 8 tokens (k-slots) per lane
     uint32_t vs[8];                               // V scale byte per token
 };
 
-template <int D>
+template <int D, int KF>
 __device__ inline Offs lane_offsets(int64_t slot0, int g, int n) {
     constexpr int EPL = D / 16;
+    constexpr int CB = KGeom<D, KF>::CB;
     Offs o;
-    o.kc = (uint32_t)((slot0 + n) * (D / 2) + (D / 8) * g);
-    o.ks = (uint32_t)((slot0 + n) * (D / 16) + (D / 64) * g);
+    o.kc = (uint32_t)((slot0 + n) * CB + (CB / 4) * g);
+    o.ks = KF ? (uint32_t)((slot0 + 4 * g) * 4) : (uint32_t)((slot0 + n) * (D / 16) + (D / 64) * g);
     o.vc = (uint32_t)((slot0 + 4 * g) * (D / 2) + (EPL / 2) * n);
     o.vs = (uint32_t)((slot0 + 4 * g) * (D / 16) + (EPL * n) / 16);
     return o;
 }
 
-template <int D>
-__device__ inline void load_k(Raw<D> &r, rsrc_t kc, rsrc_t ks, const Offs &o) {
+// Loads the K block at o: PART 0 everything; PART 1 the codes of tile 0 only; PART 2 the
+// codes of tile 1 and the scales of both tiles.
+template <int D, int KF, int PART = 0>
+__device__ inline void load_k(Raw<D, KF> &r, rsrc_t kc, rsrc_t ks, const Offs &o) {
+    constexpr int CB = KGeom<D, KF>::CB, SB = KGeom<D, KF>::SB;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const uint32_t oc = o.kc + 16 * mt * (D / 2);
-        const uint32_t os = o.ks + 16 * mt * (D / 16);
-        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, oc, 0, 0);
-        r.k[mt][0] = a[0]; r.k[mt][1] = a[1]; r.k[mt][2] = a[2]; r.k[mt][3] = a[3];
-        if constexpr (D == 256) {
-            const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(kc, oc + 16, 0, 0);
-            r.k[mt][4] = b[0]; r.k[mt][5] = b[1]; r.k[mt][6] = b[2]; r.k[mt][7] = b[3];
-            r.ks[mt] = __builtin_amdgcn_raw_buffer_load_b32(ks, os, 0, 0);
+        const uint32_t oc = o.kc + 16 * mt * CB;
+        const uint32_t os = o.ks + 16 * mt * SB;
+        if (PART == 0 || PART == mt + 1) {
+#pragma unroll
+            for (int c = 0; c < Raw<D, KF>::KW / 4; ++c) {
+                const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, oc + 16 * c, 0, 0);
+                r.k[mt][4 * c] = a[0]; r.k[mt][4 * c + 1] = a[1]; r.k[mt][4 * c + 2] = a[2]; r.k[mt][4 * c + 3] = a[3];
+            }
+        }
+        if (PART == 1) continue;
+        if constexpr (KF == 1) {
+            const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(ks, os, 0, 0);
+            r.ks[mt][0] = b[0]; r.ks[mt][1] = b[1]; r.ks[mt][2] = b[2]; r.ks[mt][3] = b[3];
+        } else if constexpr (D == 256) {
+            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b32(ks, os, 0, 0);
         } else {
-            r.ks[mt] = __builtin_amdgcn_raw_buffer_load_b16(ks, os, 0, 0);
+            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b16(ks, os, 0, 0);
         }
     }
 }
 
-template <int D>
-__device__ inline void load_v(Raw<D> &r, rsrc_t vc, rsrc_t vs, const Offs &o) {
+template <int D, int KF>
+__device__ inline void load_v(Raw<D, KF> &r, rsrc_t vc, rsrc_t vs, const Offs &o) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t dtok = 16 * (j >> 2) + (j & 3);
@@ -118,18 +132,26 @@ struct State {
     float thr[NT];           // m + kLazyMax: a block maximum above it moves m
 };
 
-template <int D>
-__device__ inline half8_t dequant_k(const Raw<D> &r, int mt, int kk) {
-    const uint32_t w = r.k[mt][kk];
-    const uint32_t sp = scale_pair((r.ks[mt] >> (8 * (kk >> 1))) & 0xFFu);
-    const u32x4_t a = {hmul2(fp4x2<0>(w), sp), hmul2(fp4x2<1>(w), sp), hmul2(fp4x2<2>(w), sp),
-                       hmul2(fp4x2<3>(w), sp)};
-    return __builtin_bit_cast(half8_t, a);
+// K fragment kk of tile mt: the lane's elements [8 kk, 8 kk + 8) of its d-range, in fp16.
+// NVFP4: e2m1 * S * 2^-8 (exact); FP8: the E4M3 values (exact), row scale applied later.
+template <int D, int KF>
+__device__ inline half8_t dequant_k(const Raw<D, KF> &r, int mt, int kk) {
+    if constexpr (KF == 1) {
+        const uint32_t w0 = r.k[mt][2 * kk], w1 = r.k[mt][2 * kk + 1];
+        const u32x4_t a = {fp8x2<0>(w0), fp8x2<1>(w0), fp8x2<0>(w1), fp8x2<1>(w1)};
+        return __builtin_bit_cast(half8_t, a);
+    } else {
+        const uint32_t w = r.k[mt][kk];
+        const uint32_t sp = scale_pair((r.ks[mt][0] >> (8 * (kk >> 1))) & 0xFFu);
+        const u32x4_t a = {hmul2(fp4x2<0>(w), sp), hmul2(fp4x2<1>(w), sp), hmul2(fp4x2<2>(w), sp),
+                           hmul2(fp4x2<3>(w), sp)};
+        return __builtin_bit_cast(half8_t, a);
+    }
 }
 
 // S^T tiles for the block: s[mt][rt] lane (g, n) = scores of tokens 16 mt + 4 g + i, row 16 rt + n.
-template <int D, int NT>
-__device__ inline void qk_block(float4_t (&s)[2][NT], const Raw<D> &r, const half8_t *qlds, int lane) {
+template <int D, int NT, int KF>
+__device__ inline void qk_block(float4_t (&s)[2][NT], const Raw<D, KF> &r, const half8_t *qlds, int lane) {
     constexpr int KK = D / 32;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -137,14 +159,24 @@ __device__ inline void qk_block(float4_t (&s)[2][NT], const Raw<D> &r, const hal
         for (int rt = 0; rt < NT; ++rt) s[mt][rt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-        const half8_t a0 = dequant_k<D>(r, 0, kk);
-        const half8_t a1 = dequant_k<D>(r, 1, kk);
+        const half8_t a0 = dequant_k<D, KF>(r, 0, kk);
+        const half8_t a1 = dequant_k<D, KF>(r, 1, kk);
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
             const half8_t qf = qlds[(rt * KK + kk) * 64 + lane];
             s[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf, s[0][rt], 0, 0, 0);
             s[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qf, s[1][rt], 0, 0, 0);
         }
+    }
+    if constexpr (KF == 1) {
+        // the keys' row scales (score element i of tile mt is token 16 mt + 4 g + i); taken
+        // before the next block's K loads reuse these registers
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[mt][rt][i] *= __builtin_bit_cast(float, r.ks[mt][i]);
     }
 }
 
@@ -155,8 +187,8 @@ struct VPrep {
     uint32_t E[4][VW], O[4][VW], SP[4];
 };
 
-template <int D>
-__device__ inline void v_prep(VPrep<D> &vp, const Raw<D> &r) {
+template <int D, int KF>
+__device__ inline void v_prep(VPrep<D> &vp, const Raw<D, KF> &r) {
     constexpr int VW = D / 128;
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
@@ -287,7 +319,7 @@ struct Lds {
     static constexpr int BYTES = Q_BYTES > MERGE_BYTES ? Q_BYTES : MERGE_BYTES;
 };
 
-template <int D, int NT, bool DevLen>
+template <int D, int NT, bool DevLen, int KF>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_waves_per_simd(NT))))
 void decode_partial_kernel(DecodeParams p) {
     constexpr int EPL = D / 16;
@@ -311,9 +343,11 @@ void decode_partial_kernel(DecodeParams p) {
     // R: this launch's rows [row0, row0 + R) of the KV head's Rt = G n_q rows
     const int R = rw.Rc, G = p.G, Rt = p.R, row0 = rw.row0;
     const int64_t base = p.seq_base[b];
+    constexpr int KCB = KGeom<D, KF>::CB, KSB = KGeom<D, KF>::SB;
     const uint32_t code_bytes = (uint32_t)(p.cap * (D / 2)), scale_bytes = (uint32_t)(p.cap * (D / 16));
-    const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * code_bytes, code_bytes);
-    const rsrc_t ks = plane_rsrc(p.ks + (int64_t)kh * scale_bytes, scale_bytes);
+    const uint32_t kcode_bytes = (uint32_t)(p.cap * KCB), kscale_bytes = (uint32_t)(p.cap * KSB);
+    const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * kcode_bytes, kcode_bytes);
+    const rsrc_t ks = plane_rsrc(p.ks + (int64_t)kh * kscale_bytes, kscale_bytes);
     const rsrc_t vc = plane_rsrc(p.vc + (int64_t)kh * code_bytes, code_bytes);
     const rsrc_t vs = plane_rsrc(p.vs + (int64_t)kh * scale_bytes, scale_bytes);
     half8_t *qlds = reinterpret_cast<half8_t *>(lds);
@@ -327,22 +361,22 @@ void decode_partial_kernel(DecodeParams p) {
     // workgroup barrier orders the stores before every wave's later loads (workgroup-scope
     // visibility of global memory: all waves share this CU's vector cache).
     if (p.k_new != nullptr && un.last) {
-        append_step_rows<D>(p, b, kh, un.L);
+        append_step_rows<D, KF>(p, b, kh, un.L);
         __syncthreads();
     }
     __builtin_amdgcn_sched_barrier(0);
-    Raw<D> r;
+    Raw<D, KF> r;
     int kb = wave;
-    Offs o = lane_offsets<D>(base + t0 + (int64_t)kBlockTokens * kb, g, n);
+    Offs o = lane_offsets<D, KF>(base + t0 + (int64_t)kBlockTokens * kb, g, n);
     constexpr uint32_t kStep = kBlockTokens * kWaves;    // tokens between a wave's blocks
     {
         const Offs o0 = kb < nblk ? o : Offs{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
-        load_k<D>(r, kc, ks, o0);
-        load_v<D>(r, vc, vs, o0);
+        load_k<D, KF>(r, kc, ks, o0);
+        load_v<D, KF>(r, vc, vs, o0);
     }
 
     // ---- Q rows -> fp16 fragments in LDS (wave rt converts row tile rt)
-    if (wave < NT) q_store<D>(p, rw, b, kh, wave, lane, qw, qlds, sm_c);
+    if (wave < NT) q_store<D, KF>(p, rw, b, kh, wave, lane, qw, qlds, sm_c);
     __syncthreads();
     float cexp[NT];
     int qi[NT];
@@ -373,8 +407,8 @@ void decode_partial_kernel(DecodeParams p) {
         // The Q fragments are re-read from LDS every block instead of being held in 32
         // registers per row tile (registers decide how many waves a SIMD holds).
         asm volatile("" ::: "memory");
-        o.kc += kStep * (D / 2);
-        o.ks += kStep * (D / 16);
+        o.kc += kStep * KCB;
+        o.ks += kStep * KSB;
         o.vc += kStep * (D / 2);
         o.vs += kStep * (D / 16);
         // The next block's loads are issued unconditionally: past the unit's last block
@@ -384,17 +418,25 @@ void decode_partial_kernel(DecodeParams p) {
         const bool has_next = kb + kWaves < nblk;
         const Offs on = has_next ? o : Offs{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
         float4_t s[2][NT];
-        qk_block<D, NT>(s, r, qlds, lane);
-        load_k<D>(r, kc, ks, on);
+        qk_block<D, NT, KF>(s, r, qlds, lane);
+        // FP8 K at two row tiles: the second tile's codes and both tiles' row scales are
+        // loaded at the end of the trip, so their 24 registers are free while the scores,
+        // probabilities and interleaved V are live (else 256 VGPRs do not hold the loop)
+        constexpr bool kSplitK = KF == 1 && NT == 2 && D == 256;
+        if constexpr (kSplitK)
+            load_k<D, KF, 1>(r, kc, ks, on);
+        else
+            load_k<D, KF>(r, kc, ks, on);
         VPrep<D> vp;
-        v_prep<D>(vp, r);
+        v_prep<D, KF>(vp, r);
         // keep the V loads below the code interleave, so they land in the registers it
         // has just read instead of fresh ones that must be copied back at the loop end
         __builtin_amdgcn_sched_barrier(0);
-        load_v<D>(r, vc, vs, on);
+        load_v<D, KF>(r, vc, vs, on);
         half8_t pa[NT];
         softmax_block<D, NT>(st, s, pa, cexp, qi, lim, g);
         pv_block<D, NT>(st, vp, pa);
+        if constexpr (kSplitK) load_k<D, KF, 2>(r, kc, ks, on);
     }
 
     // ---- merge the four waves' (o, m, l) and write the unit's partial
@@ -586,22 +628,27 @@ void decode_combine_kernel(DecodeParams p) {
     }
 }
 
-template <int D, int NT>
+template <int D, int NT, int KF>
 hipError_t launch_partial_t(const DecodeParams &p, hipStream_t s) {
     if (p.len_dev != nullptr)
-        hipLaunchKernelGGL((decode_partial_kernel<D, NT, true>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((decode_partial_kernel<D, NT, true, KF>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_partial_kernel<D, NT, false>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((decode_partial_kernel<D, NT, false, KF>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
     return hipGetLastError();
+}
+
+template <int KF>
+hipError_t launch_partial_kf(const DecodeParams &p, int D, int NT, hipStream_t s) {
+    if (D == 256) return NT == 1 ? launch_partial_t<256, 1, KF>(p, s) : launch_partial_t<256, 2, KF>(p, s);
+    if (D == 128) return NT == 1 ? launch_partial_t<128, 1, KF>(p, s) : launch_partial_t<128, 2, KF>(p, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode_partial(const DecodeParams &p, int D, int NT, hipStream_t s) {
     if (NT > 2) return launch_decode_pair(p, D, NT, s);
-    if (D == 256) return NT == 1 ? launch_partial_t<256, 1>(p, s) : launch_partial_t<256, 2>(p, s);
-    if (D == 128) return NT == 1 ? launch_partial_t<128, 1>(p, s) : launch_partial_t<128, 2>(p, s);
-    return hipErrorInvalidValue;
+    return p.k_fp8 ? launch_partial_kf<1>(p, D, NT, s) : launch_partial_kf<0>(p, D, NT, s);
 }
 
 hipError_t launch_decode_combine(const DecodeParams &p, int D, hipStream_t s) {

@@ -19,9 +19,11 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyMax = 8.0f;      // raise the softmax reference only past m + 8 (base 2)
-// Smallest score factor (see q_store). MFMA scores are below 2^27 in magnitude (|q| < 2^15
-// per element after scaling, |k_hat'| <= 6 * 448 * 2^-8 = 10.5, 256 terms), so a score times
-// this is below 2^-72.
+// Smallest score factor (see q_store). NVFP4 K: MFMA scores are below 2^27 in magnitude
+// (|q| < 2^15 per element after scaling, |k_hat'| <= 6 * 448 * 2^-8 = 10.5, 256 terms), so a
+// score times this is below 2^-72. FP8 K (K8V4): scores are below 2^32 times the key's row
+// scale (amax_row / 448), so below 2^-67 times amax_row: negligible unless K's magnitudes
+// exceed about 10^15.
 constexpr float kMinScoreScale = 1e-30f;
 
 __device__ inline half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
@@ -85,15 +87,32 @@ struct Offs {
     uint32_t kc, ks, vc, vs;
 };
 
+// Geometry of the K planes: KF = 0, NVFP4 (D/2 code bytes and D/16 E4M3 scale bytes per
+// token row); KF = 1, row-scaled FP8 E4M3 of K8V4 (D code bytes and one fp32 scale per row).
+// V planes are NVFP4 either way.
+template <int D, int KF>
+struct KGeom {
+    static constexpr int CB = KF ? D : D / 2;          // K code bytes per token row
+    static constexpr int SB = KF ? 4 : D / 16;         // K scale bytes per token row
+};
+
 // Byte offsets of a block starting at token slot slot0: lane part + slot part (32-bit:
 // a head plane is below 2^31 bytes).
-__device__ inline Offs add_slot(const Offs &lane, uint32_t slot0, int D) {
+template <int D, int KF>
+__device__ inline Offs add_slot(const Offs &lane, uint32_t slot0) {
     Offs o;
-    o.kc = lane.kc + slot0 * (uint32_t)(D / 2);
-    o.ks = lane.ks + slot0 * (uint32_t)(D / 16);
+    o.kc = lane.kc + slot0 * (uint32_t)KGeom<D, KF>::CB;
+    o.ks = lane.ks + slot0 * (uint32_t)KGeom<D, KF>::SB;
     o.vc = lane.vc + slot0 * (uint32_t)(D / 2);
     o.vs = lane.vs + slot0 * (uint32_t)(D / 16);
     return o;
+}
+
+// fp16 pair of the two E4M3 bytes in the low (SEL = 0) or high (SEL = 1) half of w: exact
+// (every E4M3 value is an fp16 value; the scale operand 1.0 leaves them unchanged).
+template <int SEL>
+__device__ inline uint32_t fp8x2(uint32_t w) {
+    return as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL != 0));
 }
 
 // Head planes are below 2^31 bytes (the capacity limit), so this offset, plus any
@@ -176,12 +195,28 @@ __device__ inline void trim_causal(Unit &un, const DecodeParams &p, const Rows &
     }
 }
 
-// The n_q rows a decode step appends for (sequence b, KV head kh) before reading
-// them: rows b n_q + r (r < n_q) of k_new / v_new, quantised with the sequence's
-// global scales by the append kernel's group quantiser and stored at slots
-// seq_base[b] + L - n_q + r. One thread per (K|V, row, group of 16). The caller
-// fences before any of its loads can touch those slots.
+// One 16-element group of a K row of a K8V4 pool: the row's scale from the maxima of its
+// D/16 groups, held by D/16 consecutive lanes aligned to D/16 (all active together), then
+// the group's 16 code bytes; the row's first lane also stores the scale.
 template <int D>
+__device__ inline void store_fp8_group(const uint32_t (&w)[8], int j, uint8_t *kc, uint8_t *ks, int64_t plane_row) {
+    uint32_t am = amax16_bits(w);
+#pragma unroll
+    for (int off = 1; off < D / 16; off <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
+    const float s = fp8_row_scale(am);
+    uint32_t c[4];
+    fp8_row_codes(w, s, c);
+    *reinterpret_cast<uint4 *>(kc + plane_row * D + 16 * j) = make_uint4(c[0], c[1], c[2], c[3]);
+    if (j == 0) reinterpret_cast<float *>(ks)[plane_row] = s;
+}
+
+// The n_q rows a decode step appends for (sequence b, KV head kh) before reading
+// them: rows b n_q + r (r < n_q) of k_new / v_new, quantised by the append kernel's
+// quantisers (NVFP4 groups with the sequence's global scales; K8V4's K rows row-scaled
+// FP8) and stored at slots seq_base[b] + L - n_q + r. One thread per (K|V, row, group of
+// 16): a row's groups are D/16 consecutive threads. The caller fences before any of its
+// loads can touch those slots.
+template <int D, int KF>
 __device__ inline void append_step_rows(const DecodeParams &p, int b, int kh, int64_t L) {
     constexpr int groups = D / 16;
     const int per_kv = p.n_q * groups;
@@ -194,11 +229,16 @@ __device__ inline void append_step_rows(const DecodeParams &p, int b, int kh, in
         const uint4 w0 = *reinterpret_cast<const uint4 *>(src);
         const uint4 w1 = *reinterpret_cast<const uint4 *>(src + 8);
         const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        uint32_t packed[2];
-        const uint32_t sc = quantize_group(w, p.gscale[(b * p.Hkv + kh) * 2 + kv], packed);
         const int64_t plane_row = (int64_t)kh * p.cap + p.seq_base[b] + L - p.n_q + r;
-        *reinterpret_cast<uint2 *>((kv ? p.vc : p.kc) + plane_row * (D / 2) + 8 * j) = make_uint2(packed[0], packed[1]);
-        (kv ? p.vs : p.ks)[plane_row * groups + j] = (uint8_t)sc;
+        if (KF == 1 && kv == 0) {
+            store_fp8_group<D>(w, j, p.kc, p.ks, plane_row);
+        } else {
+            uint32_t packed[2];
+            const uint32_t sc = quantize_group(w, p.gscale[(b * p.Hkv + kh) * 2 + kv], packed);
+            *reinterpret_cast<uint2 *>((kv ? p.vc : p.kc) + plane_row * (D / 2) + 8 * j) =
+                make_uint2(packed[0], packed[1]);
+            (kv ? p.vs : p.ks)[plane_row * groups + j] = (uint8_t)sc;
+        }
     }
 }
 
@@ -237,7 +277,7 @@ __device__ inline void q_load(const DecodeParams &p, const Rows &rw, int b, int 
     }
 }
 
-template <int D>
+template <int D, int KF>
 __device__ inline void q_store(const DecodeParams &p, const Rows &rw, int b, int kh, int rt, int lane,
                                const uint32_t (&w)[D / 8], half8_t *qlds, float *sm_c) {
     constexpr int KK = D / 32;
@@ -264,8 +304,10 @@ __device__ inline void q_store(const DecodeParams &p, const Rows &rw, int b, int
         qlds[(rt * KK + kk) * 64 + lane] = __builtin_bit_cast(half8_t, hv);
     }
     if (g == 0) {
-        const float gk = p.gscale[(b * p.Hkv + kh) * 2 + 0];
-        const float c = row < rw.Rc ? fabsf(p.sm_scale) * gk * ldexpf(1.0f, 8 - shift) * kLog2e : 0.0f;
+        // NVFP4 K: MFMA scores are of e2m1 * S * 2^-8 (times g_K); K8V4's FP8 K: of the E4M3
+        // values themselves, the row scales multiplied in per key afterwards
+        const float gk = KF ? 1.0f : p.gscale[(b * p.Hkv + kh) * 2 + 0];
+        const float c = row < rw.Rc ? fabsf(p.sm_scale) * gk * ldexpf(1.0f, (KF ? 0 : 8) - shift) * kLog2e : 0.0f;
         sm_c[row] = fmaxf(c, kMinScoreScale);
     }
 }

@@ -42,32 +42,39 @@ using namespace dev;
 // settles after its first blocks: every later move costs the whole workgroup an exchange.
 constexpr float kPairLazy = 15.0f;
 
-template <int D>
+// KF: the K format (0 NVFP4; 1 the row-scaled FP8 E4M3 K of K8V4), see KGeom.
+template <int D, int KF>
 struct PairRaw {
-    static constexpr int KW = D / 32;           // K code dwords of one 16-token tile per lane
+    static constexpr int KW = KF ? D / 16 : D / 32;   // K code dwords of one 16-token tile per lane
+    static constexpr int KS = KF ? 4 : 1;
     uint32_t k[KW];
-    uint32_t ks;                                // D/64 K scale bytes
+    uint32_t ks[KS];                            // NVFP4: D/64 K scale bytes; FP8: fp32 row scales of
+                                                // tokens 16 w + 4 g + i
     uint32_t v[8];                              // D/64 V code bytes per k-slot token
     uint32_t vs[8];                             // V scale byte per k-slot token
 };
 
-template <int D>
-__device__ inline void pair_load_k(PairRaw<D> &r, rsrc_t kc, rsrc_t ks, const Offs &o) {
-    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, o.kc, 0, 0);
-    r.k[0] = a[0]; r.k[1] = a[1]; r.k[2] = a[2]; r.k[3] = a[3];
-    if constexpr (D == 256) {
-        const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(kc, o.kc + 16, 0, 0);
-        r.k[4] = c[0]; r.k[5] = c[1]; r.k[6] = c[2]; r.k[7] = c[3];
-        r.ks = __builtin_amdgcn_raw_buffer_load_b32(ks, o.ks, 0, 0);
+template <int D, int KF>
+__device__ inline void pair_load_k(PairRaw<D, KF> &r, rsrc_t kc, rsrc_t ks, const Offs &o) {
+#pragma unroll
+    for (int c = 0; c < PairRaw<D, KF>::KW / 4; ++c) {
+        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, o.kc + 16 * c, 0, 0);
+        r.k[4 * c] = a[0]; r.k[4 * c + 1] = a[1]; r.k[4 * c + 2] = a[2]; r.k[4 * c + 3] = a[3];
+    }
+    if constexpr (KF == 1) {
+        const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(ks, o.ks, 0, 0);
+        r.ks[0] = b[0]; r.ks[1] = b[1]; r.ks[2] = b[2]; r.ks[3] = b[3];
+    } else if constexpr (D == 256) {
+        r.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(ks, o.ks, 0, 0);
     } else {
-        r.ks = __builtin_amdgcn_raw_buffer_load_b16(ks, o.ks, 0, 0);
+        r.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(ks, o.ks, 0, 0);
     }
 }
 
 // k-slot j of lane group g is token 16 (j >> 2) + 4 g + (j & 3) of the block; the lane
 // offsets already hold the 4 g.
-template <int D>
-__device__ inline void pair_load_v(PairRaw<D> &r, rsrc_t vc, rsrc_t vs, const Offs &o) {
+template <int D, int KF>
+__device__ inline void pair_load_v(PairRaw<D, KF> &r, rsrc_t vc, rsrc_t vs, const Offs &o) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t dtok = 16 * (j >> 2) + (j & 3);
@@ -80,23 +87,30 @@ __device__ inline void pair_load_v(PairRaw<D> &r, rsrc_t vc, rsrc_t vs, const Of
 }
 
 // Lane part of the byte offsets of wave w's loads, relative to the block's first slot.
-template <int D>
+template <int D, int KF>
 __device__ inline Offs pair_lane_offsets(int w, int g, int n) {
+    constexpr int CB = KGeom<D, KF>::CB;
     Offs o;
-    o.kc = (uint32_t)((16 * w + n) * (D / 2) + (D / 8) * g);
-    o.ks = (uint32_t)((16 * w + n) * (D / 16) + (D / 64) * g);
+    o.kc = (uint32_t)((16 * w + n) * CB + (CB / 4) * g);
+    o.ks = KF ? (uint32_t)((16 * w + 4 * g) * 4) : (uint32_t)((16 * w + n) * (D / 16) + (D / 64) * g);
     o.vc = (uint32_t)(4 * g * (D / 2) + (D / 32) * n + (D / 64) * w);
     o.vs = (uint32_t)(4 * g * (D / 16) + (D * n) / 256);
     return o;
 }
 
-template <int D>
-__device__ inline half8_t pair_dequant_k(const PairRaw<D> &r, int kk) {
-    const uint32_t w = r.k[kk];
-    const uint32_t sp = scale_pair((r.ks >> (8 * (kk >> 1))) & 0xFFu);
-    const u32x4_t a = {hmul2(fp4x2<0>(w), sp), hmul2(fp4x2<1>(w), sp), hmul2(fp4x2<2>(w), sp),
-                       hmul2(fp4x2<3>(w), sp)};
-    return __builtin_bit_cast(half8_t, a);
+template <int D, int KF>
+__device__ inline half8_t pair_dequant_k(const PairRaw<D, KF> &r, int kk) {
+    if constexpr (KF == 1) {
+        const uint32_t w0 = r.k[2 * kk], w1 = r.k[2 * kk + 1];
+        const u32x4_t a = {fp8x2<0>(w0), fp8x2<1>(w0), fp8x2<0>(w1), fp8x2<1>(w1)};
+        return __builtin_bit_cast(half8_t, a);
+    } else {
+        const uint32_t w = r.k[kk];
+        const uint32_t sp = scale_pair((r.ks[0] >> (8 * (kk >> 1))) & 0xFFu);
+        const u32x4_t a = {hmul2(fp4x2<0>(w), sp), hmul2(fp4x2<1>(w), sp), hmul2(fp4x2<2>(w), sp),
+                           hmul2(fp4x2<3>(w), sp)};
+        return __builtin_bit_cast(half8_t, a);
+    }
 }
 
 // V codes of k-slot pairs (2 kp, 2 kp + 1) interleaved nibble-wise: byte b of E holds
@@ -105,8 +119,8 @@ struct PairVPrep {
     uint32_t E[4], O[4], SP[4];
 };
 
-template <int D>
-__device__ inline void pair_v_prep(PairVPrep &vp, const PairRaw<D> &r) {
+template <int D, int KF>
+__device__ inline void pair_v_prep(PairVPrep &vp, const PairRaw<D, KF> &r) {
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
         const uint32_t wa = r.v[2 * kp], wb = r.v[2 * kp + 1];
@@ -129,7 +143,7 @@ struct PairLds {
     static constexpr int BIG = Q_BYTES > MERGE_BYTES ? Q_BYTES : MERGE_BYTES;
 };
 
-template <int D, int NT, bool DevLen>
+template <int D, int NT, bool DevLen, int KF>
 __global__ __attribute__((amdgpu_flat_work_group_size(128 * decode_pairs_per_wg(NT), 128 * decode_pairs_per_wg(NT)),
                           amdgpu_waves_per_eu(decode_waves_per_simd(NT))))
 void decode_pair_kernel(DecodeParams p) {
@@ -158,8 +172,10 @@ void decode_pair_kernel(DecodeParams p) {
     // R: this launch's rows [row0, row0 + R) of the KV head's Rt = G n_q rows
     const int R = rw.Rc, G = p.G, Rt = p.R, row0 = rw.row0;
     const uint32_t code_bytes = (uint32_t)(p.cap * (D / 2)), scale_bytes = (uint32_t)(p.cap * (D / 16));
-    const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * code_bytes, code_bytes);
-    const rsrc_t ks = plane_rsrc(p.ks + (int64_t)kh * scale_bytes, scale_bytes);
+    const uint32_t kcode_bytes = (uint32_t)(p.cap * KGeom<D, KF>::CB);
+    const uint32_t kscale_bytes = (uint32_t)(p.cap * KGeom<D, KF>::SB);
+    const rsrc_t kc = plane_rsrc(p.kc + (int64_t)kh * kcode_bytes, kcode_bytes);
+    const rsrc_t ks = plane_rsrc(p.ks + (int64_t)kh * kscale_bytes, kscale_bytes);
     const rsrc_t vc = plane_rsrc(p.vc + (int64_t)kh * code_bytes, code_bytes);
     const rsrc_t vs = plane_rsrc(p.vs + (int64_t)kh * scale_bytes, scale_bytes);
     half8_t *qlds = reinterpret_cast<half8_t *>(big);
@@ -174,23 +190,23 @@ void decode_pair_kernel(DecodeParams p) {
     // workgroup barrier orders the stores before every wave's later loads (workgroup-scope
     // visibility of global memory: all waves share this CU's vector cache).
     if (p.k_new != nullptr && un.last) {
-        append_step_rows<D>(p, b, kh, un.L);
+        append_step_rows<D, KF>(p, b, kh, un.L);
         __syncthreads();
     }
     __builtin_amdgcn_sched_barrier(0);
     int kb = pair;
-    const Offs lo = pair_lane_offsets<D>(w, g, n);
+    const Offs lo = pair_lane_offsets<D, KF>(w, g, n);
     const uint32_t slot_unit = (uint32_t)(p.seq_base[b] + un.t0);
     auto offs_for = [&](int blk) -> Offs {
-        return blk < nblk ? add_slot(lo, slot_unit + (uint32_t)(kBlockTokens * blk), D) : sentinel;
+        return blk < nblk ? add_slot<D, KF>(lo, slot_unit + (uint32_t)(kBlockTokens * blk)) : sentinel;
     };
-    PairRaw<D> r;
+    PairRaw<D, KF> r;
     {
         const Offs o0 = offs_for(kb);
-        pair_load_k<D>(r, kc, ks, o0);
-        pair_load_v<D>(r, vc, vs, o0);
+        pair_load_k<D, KF>(r, kc, ks, o0);
+        pair_load_v<D, KF>(r, vc, vs, o0);
     }
-    if (wave < NT) q_store<D>(p, rw, b, kh, wave, lane, qw, qlds, sm_c);
+    if (wave < NT) q_store<D, KF>(p, rw, b, kh, wave, lane, qw, qlds, sm_c);
     if (threadIdx.x < 16) (&mflag[0][0])[threadIdx.x] = 0;   // bytes of absent waves stay 0
     __syncthreads();
     float cexp[NT];
@@ -202,9 +218,9 @@ void decode_pair_kernel(DecodeParams p) {
         qi[rt] = row < R ? (row0 + row) / G : p.n_q;  // padded rows see every key (their q is 0)
     }
     // At three row tiles the first tile's Q fragments stay in registers (KK x 4 VGPRs, room
-    // left at two waves per SIMD): a third less LDS read traffic in the score stage, where the
-    // eight waves of the CU otherwise queue on LDS together.
-    constexpr int kQReg = NT == 3 ? 1 : 0;
+    // left at two waves per SIMD with NVFP4 K): a third less LDS read traffic in the score
+    // stage, where the eight waves of the CU otherwise queue on LDS together.
+    constexpr int kQReg = (NT == 3 && KF == 0) ? 1 : 0;
     half8_t qreg[kQReg ? KK : 1];
 #pragma unroll
     for (int kk = 0; kk < (kQReg ? KK : 0); ++kk) qreg[kk] = qlds[kk * 64 + lane];
@@ -275,13 +291,21 @@ void decode_pair_kernel(DecodeParams p) {
         for (int rt = 0; rt < NT; ++rt) s[rt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const half8_t a = pair_dequant_k<D>(r, kk);
+            const half8_t a = pair_dequant_k<D, KF>(r, kk);
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt)
                 s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, rt < kQReg ? qreg[kk] : qlds[(rt * KK + kk) * 64 + lane],
                                                                s[rt], 0, 0, 0);
         }
-        pair_load_k<D>(r, kc, ks, offs_for(pair + kPairs * (j + 1)));
+        if constexpr (KF == 1) {
+            // the keys' row scales (score element i is token 16 w + 4 g + i), taken before the
+            // next block's K loads reuse these registers
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[rt][i] *= __builtin_bit_cast(float, r.ks[i]);
+        }
+        pair_load_k<D, KF>(r, kc, ks, offs_for(pair + kPairs * (j + 1)));
         const int lim = pair + kPairs * j < nblk ? lim0 - (int)kPairStep * j : -(1 << 30);
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
@@ -385,15 +409,15 @@ void decode_pair_kernel(DecodeParams p) {
             read_p(j, pa);
         }
         pv_block(pa, vprep);
-        pair_v_prep<D>(vprep, r);
+        pair_v_prep<D, KF>(vprep, r);
         __builtin_amdgcn_sched_barrier(0);
-        pair_load_v<D>(r, vc, vs, offs_for(pair + kPairs * (j + 2)));
+        pair_load_v<D, KF>(r, vc, vs, offs_for(pair + kPairs * (j + 2)));
         if (do_next) start_block(j + 1);
     };
 
     start_block(0);
-    pair_v_prep<D>(vprep, r);
-    pair_load_v<D>(r, vc, vs, offs_for(pair + kPairs));
+    pair_v_prep<D, KF>(vprep, r);
+    pair_load_v<D, KF>(r, vc, vs, offs_for(pair + kPairs));
     for (int j = 0; j < iters - 1; ++j) trip(j, true);
     trip(iters - 1, false);
 
@@ -469,30 +493,35 @@ void decode_pair_kernel(DecodeParams p) {
     }
 }
 
-template <int D, int NT>
+template <int D, int NT, int KF>
 hipError_t launch_pair_t(const DecodeParams &p, hipStream_t s) {
     if (p.len_dev != nullptr)
-        hipLaunchKernelGGL((decode_pair_kernel<D, NT, true>), dim3(p.units, p.grid_y), dim3(128 * decode_pairs_per_wg(NT)), 0, s, p);
+        hipLaunchKernelGGL((decode_pair_kernel<D, NT, true, KF>), dim3(p.units, p.grid_y), dim3(128 * decode_pairs_per_wg(NT)), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_pair_kernel<D, NT, false>), dim3(p.units, p.grid_y), dim3(128 * decode_pairs_per_wg(NT)), 0, s, p);
+        hipLaunchKernelGGL((decode_pair_kernel<D, NT, false, KF>), dim3(p.units, p.grid_y), dim3(128 * decode_pairs_per_wg(NT)), 0, s, p);
     return hipGetLastError();
+}
+
+template <int KF>
+hipError_t launch_pair_kf(const DecodeParams &p, int D, int NT, hipStream_t s) {
+    if (D == 256) {
+        switch (NT) {
+            case 3: return launch_pair_t<256, 3, KF>(p, s);
+            case 4: return launch_pair_t<256, 4, KF>(p, s);
+        }
+    } else if (D == 128) {
+        switch (NT) {
+            case 3: return launch_pair_t<128, 3, KF>(p, s);
+            case 4: return launch_pair_t<128, 4, KF>(p, s);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode_pair(const DecodeParams &p, int D, int NT, hipStream_t s) {
-    if (D == 256) {
-        switch (NT) {
-            case 3: return launch_pair_t<256, 3>(p, s);
-            case 4: return launch_pair_t<256, 4>(p, s);
-        }
-    } else if (D == 128) {
-        switch (NT) {
-            case 3: return launch_pair_t<128, 3>(p, s);
-            case 4: return launch_pair_t<128, 4>(p, s);
-        }
-    }
-    return hipErrorInvalidValue;
+    return p.k_fp8 ? launch_pair_kf<1>(p, D, NT, s) : launch_pair_kf<0>(p, D, NT, s);
 }
 
 }  // namespace nvfp4

@@ -57,6 +57,7 @@ struct SplitPlan {
 struct DecodeParams {
     uint8_t *kc, *ks, *vc, *vs;          // pool planes (written only by the step's own append)
     int64_t cap;
+    int32_t k_fp8;                       // K planes: 0 NVFP4; 1 row-scaled FP8 E4M3 (K8V4)
     const float *gscale;                 // [B][Hkv][2]
     const uint16_t *q;                   // bf16 [B][n_q][Hq][D]
     const uint16_t *k_new, *v_new;       // bf16 [B n_q][Hkv][D] rows to append first, or null
@@ -83,6 +84,7 @@ struct AppendParams {
     const float *gscale;                 // [B][Hkv][2]
     uint8_t *kc, *ks, *vc, *vs;
     int64_t cap;
+    int32_t k_fp8;                       // K planes: 0 NVFP4; 1 row-scaled FP8 E4M3 (K8V4)
     int32_t B, Hkv, D;
     int64_t rows;                        // sum of n_new
     int64_t row_start[kMaxSeqs + 1];     // prefix sums of n_new

@@ -43,16 +43,23 @@ __device__ inline uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_
 __device__ inline int e4m3_sig(int c) { return (c & 7) | (c >= 8 ? 8 : 0); }
 __device__ inline int e4m3_ex(int c) { return c >= 8 ? (c >> 3) : 1; }
 
-// Nearest E4M3 code to amax / (6 g), ties to even, saturating; amax > 0, g > 0.
-__device__ inline int e4m3_code_exact(double amax, double gd) {
-    const double q = fmin(amax * __builtin_amdgcn_rcp(6.0 * gd), 448.0);
+// Nearest E4M3 code to the real a / b, ties to even, saturating at 448; a >= 0, b > 0,
+// rcp_b an approximation of 1 / b (relative error far below E4M3's 1/32 half-gap), and the
+// product of b with a 5-bit midpoint exact in fp64 (b has at most 48 significant bits).
+__device__ inline int e4m3_nearest(double a, double b, double rcp_b) {
+    const double q = fmin(a * rcp_b, 448.0);
     const float q32 = (float)q;
     // Largest code whose value is at most q32 (values are monotone in the bits).
     const int c = q32 < 0.015625f ? (int)(q32 * 512.0f) : (int)(f32_bits(q32) >> 20) - 960;
-    // m(c, c+1) * 6g = (2 sig + 1) 2^(ex - 11) * 6g, exact.
-    const double mid = ldexp((double)(12 * e4m3_sig(c) + 6) * gd, e4m3_ex(c) - 11);
-    const int up = amax > mid || (amax == mid && (c & 1));   // tie: to the even one of c, c+1
+    // m(c, c+1) * b = (2 sig + 1) 2^(ex - 11) * b, exact.
+    const double mid = ldexp((double)(2 * e4m3_sig(c) + 1) * b, e4m3_ex(c) - 11);
+    const int up = a > mid || (a == mid && (c & 1));         // tie: to the even one of c, c+1
     return min(c + up, 0x7E);
+}
+
+// Nearest E4M3 code to amax / (6 g), ties to even, saturating; amax > 0, g > 0 (6 g is exact).
+__device__ inline int e4m3_code_exact(double amax, double gd) {
+    return e4m3_nearest(amax, 6.0 * gd, __builtin_amdgcn_rcp(6.0 * gd));
 }
 
 // Both 16-bit lanes = the threshold for "a > T" (strict) or "a >= T".
@@ -131,6 +138,40 @@ __device__ inline uint32_t quantize_group(const uint32_t (&w)[8], float g, uint3
         packed[h] = e2m1_pair<0>(P[4 * h + 0], u) | e2m1_pair<1>(P[4 * h + 1], u) |
                     e2m1_pair<2>(P[4 * h + 2], u) | e2m1_pair<3>(P[4 * h + 3], u);
     return (uint32_t)sc;
+}
+
+// ---- row-scaled FP8 E4M3 (the K rows of K8V4) ----------------------------------------
+// A row of D bf16 values gets one fp32 scale s = fp32(amax_row / 448) (the fp64 quotient
+// rounded to fp32 is the correctly rounded fp32 quotient) and element codes sign << 7 |
+// the E4M3 value nearest the exact real |x| / s (e4m3_nearest: s has 24 significant bits,
+// so every midpoint product is exact in fp64). s == 0 gives zero magnitudes.
+
+// Largest bf16 magnitude bit pattern among 16 elements (w: element 2k in the low half of
+// word k); magnitudes order like their bit patterns.
+__device__ inline uint32_t amax16_bits(const uint32_t (&w)[8]) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mx = pk_max16(mx, w[k] & 0x7FFF7FFFu);
+    return max(mx & 0xFFFFu, mx >> 16);
+}
+
+__device__ inline float fp8_row_scale(uint32_t amax_bits) {
+    return (float)((double)__builtin_bit_cast(float, amax_bits << 16) / 448.0);
+}
+
+// 16 elements of a row with row scale s -> 16 code bytes (element e in byte e of out).
+__device__ inline void fp8_row_codes(const uint32_t (&w)[8], float s, uint32_t (&out)[4]) {
+    const double sd = (double)s;
+    const double rs = __builtin_amdgcn_rcp(sd);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = 0u;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const double a = (double)__builtin_bit_cast(float, (h & 0x7FFFu) << 16);
+        const int c = s > 0.0f ? e4m3_nearest(a, sd, rs) : 0;
+        out[e >> 2] |= ((uint32_t)c | ((h >> 8) & 0x80u)) << (8 * (e & 3));
+    }
 }
 
 }  // namespace dev

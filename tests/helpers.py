@@ -24,7 +24,7 @@ class OracleRun:
         self.q = workloads.queries(w) if q is None else q
         ku, vu = workloads.as_u16(self.k), workloads.as_u16(self.v)
         self.g = oracle.calibrate(ku, vu, w.seq_lens)
-        self.cache = oracle.Cache(w.num_kv_heads, w.head_dim, w.capacity)
+        self.cache = oracle.Cache(w.num_kv_heads, w.head_dim, w.capacity, kv_format=w.kv_format)
         oracle.append(self.cache, ku, vu, self.g, w.seq_base, [0] * w.batch, list(w.seq_lens), nthreads)
         self.nthreads = nthreads
 
@@ -57,7 +57,7 @@ def gpu_run(w: workloads.Workload, k: torch.Tensor, v: torch.Tensor, q: torch.Te
     """Calibrate, append and decode on the GPU through the C ABI. Returns (pool, g, out)."""
     import quantized_kv_decode_amd as qk
     dev = "cuda"
-    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev)
+    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev, kv_format=w.kv_format)
     kd, vd = k.to(dev), v.to(dev)
     g = qk.calibrate(pool, kd, vd, list(w.seq_lens))
     if chunk_rows is None:
@@ -81,13 +81,16 @@ def gpu_run(w: workloads.Workload, k: torch.Tensor, v: torch.Tensor, q: torch.Te
 
 
 def assert_planes_equal(pool, cache: oracle.Cache):
+    """Every plane byte for byte (K8V4's fp32 row scales compared as bit patterns)."""
     for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
         got = getattr(pool, name).cpu().numpy()
         ref = getattr(cache, name)
+        if got.dtype == np.float32:
+            got, ref = got.view(np.uint32), ref.view(np.uint32)
         if not np.array_equal(got, ref):
             bad = np.argwhere(got != ref)
             i = tuple(bad[0])
-            raise AssertionError(f"{name}: {len(bad)} bytes differ; first at {i}: gpu {got[i]:#04x} oracle {ref[i]:#04x}")
+            raise AssertionError(f"{name}: {len(bad)} values differ; first at {i}: gpu {got[i]:#x} oracle {ref[i]:#x}")
 
 
 def max_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -37,3 +37,28 @@ extern "C" void quantize_groups(const uint16_t *x, long n_groups, const float *g
         for (int k = 0; k < 8; ++k) codes[8 * i + k] = (uint8_t)(packed[k >> 2] >> (8 * (k & 3)));
     }
 }
+
+// Row-scaled FP8 E4M3 (K8V4's K rows): x n_rows x D bf16; codes n_rows x D; scales n_rows.
+// The row maximum is reduced over the row's 16-element groups as the device reduces it
+// across the lanes that hold them.
+extern "C" void quantize_rows_fp8(const uint16_t *x, long n_rows, int D, uint8_t *codes, float *scales, double eps) {
+    rcp_eps = eps;
+    for (long r = 0; r < n_rows; ++r) {
+        uint32_t amax = 0;
+        for (int j = 0; j < D / 16; ++j) {
+            uint32_t w[8];
+            for (int k = 0; k < 8; ++k)
+                w[k] = x[r * D + 16 * j + 2 * k] | ((uint32_t)x[r * D + 16 * j + 2 * k + 1] << 16);
+            amax = max(amax, nvfp4::dev::amax16_bits(w));
+        }
+        const float s = nvfp4::dev::fp8_row_scale(amax);
+        scales[r] = s;
+        for (int j = 0; j < D / 16; ++j) {
+            uint32_t w[8], out[4];
+            for (int k = 0; k < 8; ++k)
+                w[k] = x[r * D + 16 * j + 2 * k] | ((uint32_t)x[r * D + 16 * j + 2 * k + 1] << 16);
+            nvfp4::dev::fp8_row_codes(w, s, out);
+            for (int e = 0; e < 16; ++e) codes[r * D + 16 * j + e] = (uint8_t)(out[e >> 2] >> (8 * (e & 3)));
+        }
+    }
+}

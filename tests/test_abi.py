@@ -251,3 +251,21 @@ def test_split_plan_caps_unit_length(lib):
     # at or below the cap nothing changes: one unit per (sequence, head)
     got = lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 8, qk._i64([32768] * 8), 1, 32)
     assert got == al(256 * 128 * 4) + 2 * al(256 * 4)
+
+
+def test_kv_format_validation(lib):
+    """kv_format must be NVFP4 (0) or K8V4 (1); a K8V4 pool's K code plane (head_dim bytes
+    a row) must also stay below 2^31 bytes per head."""
+    import quantized_kv_decode_amd as qk
+    d = _desc(qk)
+    d.kv_format = 2
+    assert _call_decode(qk, lib, d) == qk.EINVAL
+    assert "kv_format" in lib.nvfp4_last_error().decode()
+    d = _desc(qk, cap=(2 ** 31 - 1) // 256 + 1)                 # fine for NVFP4 (128 B rows) ...
+    d.kv_format = 1
+    assert _call_decode(qk, lib, d) == qk.EUNSUPPORTED          # ... too large for FP8 K (256 B rows)
+    d.kv_format = 0
+    assert lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([100]), 1, 24) > 0
+    d = _desc(qk)
+    d.kv_format = 1
+    assert lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([100]), 1, 24) > 0

@@ -157,7 +157,7 @@ def test_decode_step_equals_append_then_decode(qk, shape):
     say("decode step", shape)
     ref = OracleRun(w)
     kd, vd = ref.k.cuda(), ref.v.cuda()
-    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device="cuda")
+    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device="cuda", kv_format=w.kv_format)
     g = qk.calibrate(pool, kd, vd, list(w.seq_lens))
     pre = [L - w.n_q for L in w.seq_lens]
     sl = lambda t, lo, hi: torch.cat([t[w.seq_base[b] + lo[b]:w.seq_base[b] + hi[b]] for b in range(w.batch)])
@@ -183,7 +183,7 @@ def test_decode_step_equals_append_then_decode(qk, shape):
 def _spaced_pool(qk, w, max_len):
     """A pool in which sequence b owns slots [base[b], base[b] + max_len[b]): room to grow."""
     base = [int(x) for x in np.concatenate([[0], np.cumsum(max_len)[:-1]])]
-    return qk.KVPool(w.num_kv_heads, w.head_dim, int(sum(max_len)), device="cuda"), base
+    return qk.KVPool(w.num_kv_heads, w.head_dim, int(sum(max_len)), device="cuda", kv_format=w.kv_format), base
 
 
 def _seq_rows(t, w, lo, hi):
@@ -452,7 +452,7 @@ def _full_step(qk, w, ref):
     through nvfp4_decode_step_dev_len with the lengths in device memory (bound = length).
     Returns (pool, g, out_step, out_dev_len)."""
     dev = "cuda"
-    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev)
+    pool = qk.KVPool(w.num_kv_heads, w.head_dim, w.capacity, device=dev, kv_format=w.kv_format)
     kd, vd = ref.k.to(dev), ref.v.to(dev)
     lens = list(w.seq_lens)
     g = qk.calibrate(pool, kd, vd, lens)

@@ -24,6 +24,9 @@ CSRC = os.path.join(os.path.dirname(HERE), "quantized_kv_decode_amd", "csrc")
 CLANG = "/opt/rocm/llvm/bin/clang++"
 
 
+run_fp8_holder = []
+
+
 @pytest.fixture(scope="module")
 def host_quantizer(tmp_path_factory):
     cxx = CLANG if os.path.exists(CLANG) else shutil.which("clang++")
@@ -35,6 +38,18 @@ def host_quantizer(tmp_path_factory):
     lib = ctypes.CDLL(out)
     lib.quantize_groups.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_double]
+
+    lib.quantize_rows_fp8.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_double]
+
+    def run_fp8(x, eps):
+        x = np.ascontiguousarray(x, np.uint16)
+        n, D = x.shape
+        codes = np.zeros((n, D), np.uint8)
+        scales = np.zeros(n, np.float32)
+        lib.quantize_rows_fp8(x.ctypes.data, n, D, codes.ctypes.data, scales.ctypes.data, eps)
+        return codes, scales
+    run_fp8_holder.append(run_fp8)
 
     def run(x, g, eps):
         x = np.ascontiguousarray(x, np.uint16)
@@ -101,3 +116,59 @@ def test_groups_on_midpoints(host_quantizer):
         x[:, j] = (bf16_down(t * Sg) + rng.integers(0, 2, n)) & 0x7FFF
         x[:, j] |= (rng.integers(0, 2, n) << 15).astype(np.uint16)
     check(host_quantizer, x, g)
+
+
+# ---- row-scaled FP8 E4M3 (K8V4's K rows) ---------------------------------------------------
+def check_fp8(x):
+    rc, rs = oracle.quantize_rows_fp8(x)
+    for eps in (0.0, 2.0 ** -20, -2.0 ** -20, 2.0 ** -12, -2.0 ** -12):
+        c, s = run_fp8_holder[0](x, eps)
+        assert np.array_equal(s.view(np.uint32), rs.view(np.uint32)), f"eps {eps}: row scales differ"
+        bad = np.nonzero((c != rc).any(1))[0]
+        assert bad.size == 0, f"eps {eps}: {bad.size} rows differ, first {bad[0]}"
+
+
+def test_fp8_rows_every_bf16_value_as_row_max(host_quantizer):
+    """Every positive finite bf16 value as a row's maximum (so every row scale that can occur),
+    with the row's other elements at fixed fractions of it that straddle E4M3 midpoints."""
+    mags = np.arange(1, 0x7F80, dtype=np.uint32)
+    D = 128
+    x = np.zeros((mags.size, D), np.uint16)
+    x[:, 0] = mags
+    f = np.frombuffer((mags << 16).astype(np.uint32).tobytes(), np.float32).astype(np.float64)
+    fr = [0.999, 0.5, 0.4375, 0.1, 1 / 3, 2.0 ** -7, 0.0023, 0.03125 * 1.0625, 3 * 2.0 ** -19, 0.77]
+    for k, t in enumerate(fr):
+        v = (f * t).astype(np.float32)
+        b = (np.frombuffer(v.tobytes(), np.uint32) >> 16).astype(np.uint16)   # truncated to bf16
+        x[:, 1 + k] = b | (0x8000 if k % 2 else 0)
+    check_fp8(x)
+
+
+def test_fp8_rows_on_midpoints(host_quantizer):
+    """Rows whose scale is a power of two (amax = 448 * 2^k) and whose elements sit on every E4M3
+    midpoint and one bf16 step either side of it."""
+    e4 = [oracle.e4m3_value(c) for c in range(127)]
+    rows = []
+    for k in (-20, -6, 0, 5, 17):
+        mids = np.array([(e4[i] + e4[i + 1]) / 2 * 2.0 ** k for i in range(126)], np.float32)
+        mb = (np.frombuffer(mids.tobytes(), np.uint32) >> 16).astype(np.uint16)
+        vals = np.concatenate([mb, mb + 1, mb - 1]).astype(np.uint16)
+        for i in range(0, vals.size, 255):
+            row = np.zeros(256, np.uint16)
+            top = np.array([448 * 2.0 ** k], np.float32)
+            row[0] = (np.frombuffer(top.tobytes(), np.uint32) >> 16)[0]
+            chunk = vals[i:i + 255]
+            row[1:1 + chunk.size] = chunk
+            rows.append(row)
+    check_fp8(np.stack(rows))
+
+
+def test_fp8_rows_random_and_edge(host_quantizer):
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((500, 256)) * 10.0 ** rng.uniform(-30, 30, (500, 1))).astype(np.float32)
+    xb = (np.frombuffer(x.tobytes(), np.uint32) >> 16).astype(np.uint16).reshape(500, 256)
+    edge = np.zeros((4, 256), np.uint16)
+    edge[1, :] = 0x8000                                        # all -0
+    edge[2, 5] = 0x0001                                        # smallest bf16 subnormal as the max
+    edge[3, 7] = 0x7F7F                                        # largest finite bf16
+    check_fp8(np.concatenate([xb, edge]))
