@@ -7,11 +7,15 @@
 // the visible keys, with k_hat = e2m1 * S * g_K and v_hat = e2m1 * S * g_V.
 //
 // Work decomposition. A unit is (sequence b, KV head kh, token range); one
-// 256-thread workgroup runs one unit, its four waves taking alternate 32-token
-// blocks. Every query row that reads KV head kh -- GQA group G times n_q query
+// workgroup runs one unit, each wave taking whole 32-token blocks: at one row tile
+// four waves (one per SIMD) take alternate blocks; at two row tiles eight waves (two
+// per SIMD, 256 VGPRs each) claim the unit's blocks one at a time from a counter in
+// LDS, since the hardware serves the older wave of a SIMD first and a fixed split
+// left the younger ones finishing alone (the partition, and with it the fp16 rounding
+// reference of each wave, then depends on timing: results agree to rounding, not bit
+// for bit). Every query row that reads KV head kh -- GQA group G times n_q query
 // tokens, padded to NT tiles of 16 -- shares each KV block, so a block is loaded
-// and dequantised once for all of them. This kernel serves one or two row tiles
-// (up to 32 rows: at two, 256 VGPRs, two waves per SIMD); three or four go to the
+// and dequantised once for all of them. Three or four row tiles go to the
 // wave-pair kernel, whose waves split each block.
 //
 // Per 32-token block and wave (MFMA v_mfma_f32_16x16x32_f16, lane l = 16 g + n):
@@ -320,14 +324,18 @@ struct Lds {
 };
 
 template <int D, int NT, bool DevLen, int KF>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(decode_waves_per_simd(NT))))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * decode_partial_waves(NT), 64 * decode_partial_waves(NT)),
+                          amdgpu_waves_per_eu(decode_waves_per_simd(NT))))
 void decode_partial_kernel(DecodeParams p) {
     constexpr int EPL = D / 16;
+    constexpr int W = decode_partial_waves(NT);
+    constexpr bool kClaim = NT == 2;       // waves claim blocks (else a fixed stride of W)
     using LD = Lds<D, NT>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LD::BYTES];
     __shared__ float sm_c[kMaxRows];
-    __shared__ float sm_m[kWaves][kMaxRows];
-    __shared__ float sm_l[kWaves][kMaxRows];
+    __shared__ float sm_m[W][kMaxRows];
+    __shared__ float sm_l[W][kMaxRows];
+    __shared__ uint32_t next_blk;          // the unit's next unclaimed block (kClaim)
 
     const int u = blockIdx.x;
     Unit un = unit_of<DevLen>(p, u);
@@ -367,13 +375,18 @@ void decode_partial_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
     Raw<D, KF> r;
     int kb = wave;
-    Offs o = lane_offsets<D, KF>(base + t0 + (int64_t)kBlockTokens * kb, g, n);
-    constexpr uint32_t kStep = kBlockTokens * kWaves;    // tokens between a wave's blocks
+    const Offs lo = lane_offsets<D, KF>(0, g, n);
+    const uint32_t slot_unit = (uint32_t)(base + t0);
+    auto offs_of = [&](int blk) -> Offs {
+        return blk < nblk ? add_slot<D, KF>(lo, slot_unit + (uint32_t)(kBlockTokens * blk))
+                          : Offs{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
+    };
     {
-        const Offs o0 = kb < nblk ? o : Offs{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
+        const Offs o0 = offs_of(kb);
         load_k<D, KF>(r, kc, ks, o0);
         load_v<D, KF>(r, vc, vs, o0);
     }
+    if (kClaim && threadIdx.x == 0) next_blk = W;
 
     // ---- Q rows -> fp16 fragments in LDS (wave rt converts row tile rt)
     if (wave < NT) q_store<D, KF>(p, rw, b, kh, wave, lane, qw, qlds, sm_c);
@@ -402,21 +415,21 @@ void decode_partial_kernel(DecodeParams p) {
     // loads are issued once this block's K is in the S^T tiles, its V loads once this
     // block's V codes are interleaved, so they overlap the softmax and PV work.
     // offset limit of the first block of this wave relative to L - n_q (32-bit: tokens < 2^31)
-    int lim = (int)(L - p.n_q - t0) - kBlockTokens * kb;
-    for (; kb < nblk; kb += kWaves, lim -= (int)kStep) {
-        // The Q fragments are re-read from LDS every block instead of being held in 32
-        // registers per row tile (registers decide how many waves a SIMD holds).
+    // Blocks: wave w starts with block w; then, at two row tiles, each wave claims the next
+    // unclaimed block (one LDS atomic per block, issued a block ahead of its loads), at one
+    // row tile it steps by W (a fixed partition: the result is deterministic).
+    while (kb < nblk) {
         asm volatile("" ::: "memory");
-        o.kc += kStep * KCB;
-        o.ks += kStep * KSB;
-        o.vc += kStep * (D / 2);
-        o.vs += kStep * (D / 16);
-        // The next block's loads are issued unconditionally: past the unit's last block
-        // they take an offset beyond every plane, which the buffer unit answers with zeros
-        // without a memory access. (A conditional load makes the loaded registers a
-        // two-way merge, which costs register copies and a wait for the fresh loads.)
-        const bool has_next = kb + kWaves < nblk;
-        const Offs on = has_next ? o : Offs{kPastPlane, kPastPlane, kPastPlane, kPastPlane};
+        int kn;
+        if constexpr (kClaim) {
+            uint32_t nx = 0;
+            if (lane == 0) nx = atomicAdd(&next_blk, 1u);
+            kn = __builtin_amdgcn_readfirstlane((int)nx);
+        } else {
+            kn = kb + W;
+        }
+        const Offs on = offs_of(kn);
+        const int lim = (int)(L - p.n_q - t0) - kBlockTokens * kb;
         float4_t s[2][NT];
         qk_block<D, NT, KF>(s, r, qlds, lane);
         // FP8 K at two row tiles: the second tile's codes and both tiles' row scales are
@@ -437,6 +450,7 @@ void decode_partial_kernel(DecodeParams p) {
         softmax_block<D, NT>(st, s, pa, cexp, qi, lim, g);
         pv_block<D, NT>(st, vp, pa);
         if constexpr (kSplitK) load_k<D, KF, 2>(r, kc, ks, on);
+        kb = kn;
     }
 
     // ---- merge the four waves' (o, m, l) and write the unit's partial
@@ -456,7 +470,7 @@ void decode_partial_kernel(DecodeParams p) {
             const int row = 16 * rt + 4 * g + i;
             float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][row]);
+            for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][row]);
             const float mw = sm_m[wave][row];
             const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
 #pragma unroll
@@ -467,12 +481,39 @@ void decode_partial_kernel(DecodeParams p) {
     float *ws_o = p.ws_o + ((int64_t)u * Rt + row0) * D;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
+        if constexpr (W == 8) {
+            // waves 4..7 hand their rows to waves 0..3 through the merge buffer first
+            if (wave >= 4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float *dst = &buf[wave - 4][4 * g + i][EPL * n];
+#pragma unroll
+                    for (int dt = 0; dt < EPL; dt += 4)
+                        *reinterpret_cast<float4_t *>(dst + dt) = float4_t{st.acc[rt][dt][i], st.acc[rt][dt + 1][i],
+                                                                           st.acc[rt][dt + 2][i], st.acc[rt][dt + 3][i]};
+                }
+            }
+            __syncthreads();
+            if (wave < 4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float *src = &buf[wave][4 * g + i][EPL * n];
+#pragma unroll
+                    for (int dt = 0; dt < EPL; dt += 4) {
+                        const float4_t v = *reinterpret_cast<const float4_t *>(src + dt);
+                        st.acc[rt][dt][i] += v[0]; st.acc[rt][dt + 1][i] += v[1];
+                        st.acc[rt][dt + 2][i] += v[2]; st.acc[rt][dt + 3][i] += v[3];
+                    }
+                }
+            }
+            __syncthreads();
+        }
         // Only rows below R are stored. Lane n's D/16 values sit at a stride of D/16 floats
         // from lane n + 1's, so lanes n, n + 2, ... share LDS banks; rotating the order of the
         // 4-float chunks by n / 2 spreads them over the banks.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (16 * rt + 4 * g + i < R) {
+            if (wave < 4 && 16 * rt + 4 * g + i < R) {
                 float *dst = &buf[wave][4 * g + i][EPL * n];
 #pragma unroll
                 for (int c = 0; c < EPL / 4; ++c) {
@@ -488,7 +529,7 @@ void decode_partial_kernel(DecodeParams p) {
         }
         __syncthreads();
         const int rows = min(16, R - 16 * rt);
-        for (int e = threadIdx.x; e < rows * D; e += 256) {
+        for (int e = threadIdx.x; e < rows * D; e += 64 * W) {
             const int r16 = e / D, d = e - r16 * D;
             float sum = 0.f;
 #pragma unroll
@@ -500,9 +541,9 @@ void decode_partial_kernel(DecodeParams p) {
     if ((int)threadIdx.x < R) {
         const int row = threadIdx.x;
         float M = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][row]);
+        for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][row]);
         float Ls = 0.f;
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             const float mw = sm_m[w][row];
             if (mw != -INFINITY) Ls += exp2f(mw - M) * sm_l[w][row];
         }
@@ -631,9 +672,11 @@ void decode_combine_kernel(DecodeParams p) {
 template <int D, int NT, int KF>
 hipError_t launch_partial_t(const DecodeParams &p, hipStream_t s) {
     if (p.len_dev != nullptr)
-        hipLaunchKernelGGL((decode_partial_kernel<D, NT, true, KF>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((decode_partial_kernel<D, NT, true, KF>), dim3(p.units, p.grid_y),
+                           dim3(64 * decode_partial_waves(NT)), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_partial_kernel<D, NT, false, KF>), dim3(p.units, p.grid_y), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((decode_partial_kernel<D, NT, false, KF>), dim3(p.units, p.grid_y),
+                           dim3(64 * decode_partial_waves(NT)), 0, s, p);
     return hipGetLastError();
 }
 

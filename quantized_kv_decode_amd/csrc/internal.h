@@ -30,13 +30,16 @@ constexpr int decode_waves_per_simd(int /*NT*/) { return 2; }
 // later-dispatched ones ran slower and set the kernel's end, and one workgroup halves the
 // partials (mtp_verify step 58.9 -> 56.5 us).
 constexpr int decode_pairs_per_wg(int /*NT*/) { return 4; }
-// Units the split planner gives each CU. One row tile: one, although two such workgroups
-// fit -- half as many, twice as long units pay the per-unit start and merge half as often
-// (decode at 2 x 32k tokens: partial 21.6 -> 20.2 us; 600k: 123.1 -> 121.7 us). Two row
-// tiles: two, one per resident workgroup (three sessions of 330k-470k tokens, 24 rows:
-// partial 268.8 us with one unit per CU, 261.4 with two, 271.8 with four). Three or four:
-// one 8-wave workgroup.
-constexpr int decode_units_per_cu(int NT) { return NT == 2 ? 2 : 1; }
+// Units the split planner gives each CU: one. One row tile: a 4-wave workgroup, although
+// two such workgroups fit -- half as many, twice as long units pay the per-unit start and
+// merge half as often (decode at 2 x 32k tokens: partial 21.6 -> 20.2 us; 600k: 123.1 ->
+// 121.7 us). Two row tiles: one 8-wave workgroup (two waves per SIMD) whose waves claim the
+// unit's blocks one at a time; as two 4-wave workgroups with static blocks, the one
+// dispatched second ran ~40% slower and finished alone (three sessions of 330k-470k tokens,
+// 24 rows: step 259.4 -> 254.4 us). Three or four: one 8-wave pair-kernel workgroup.
+constexpr int decode_units_per_cu(int /*NT*/) { return 1; }
+// Waves per workgroup of the one-wave-per-block kernel (one or two row tiles).
+constexpr int decode_partial_waves(int NT) { return NT == 2 ? 8 : 4; }
 
 // Split-K plan: sequence b is cut into n_split[b] units of split_len[b] tokens
 // (a multiple of kBlockTokens) for each KV head; the last unit ends at the

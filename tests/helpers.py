@@ -143,3 +143,23 @@ def adversarial_rows(D=256):
     flat = np.zeros((rows * per_row, 16), np.uint16)
     flat[:n] = np.stack(groups)
     return flat.reshape(rows, D)
+
+
+def deterministic(w) -> bool:
+    """Whether the decode kernels give the same output bits on every run for this shape: one
+    row tile (up to 16 query rows per KV head) and the wave-pair kernel (33-64 rows) process
+    fixed block partitions; at two row tiles (17-32 rows, and the 32-row chunks above 64 rows)
+    the waves claim blocks as they free up, so the partition -- and the fp16 rounding of the
+    probabilities against each wave's reference -- depends on timing."""
+    R = w.rows
+    return R <= 16 or 33 <= R <= 64
+
+
+def assert_same_output(a: torch.Tensor, b: torch.Tensor, w, vmax: float):
+    """Outputs of two runs of the same step: identical bits where the kernels are
+    deterministic, else within the attention tolerance of each other."""
+    if deterministic(w):
+        assert torch.equal(a, b)
+    else:
+        err = (a.float() - b.float()).abs().max().item()
+        assert err <= TOL_REL * vmax, (err, TOL_REL * vmax)

@@ -189,24 +189,24 @@ def test_decode_step_dev_len_validation_codes(lib):
 def test_wide_row_counts_plan_like_their_chunks(lib):
     """65..128 rows per KV head run as 32-row chunks side by side (grid y) over one split
     plan: 96 rows (n_q = 16, G = 6) and 72 rows (32 + 32 + 8) are three chunks, so of the
-    512 workgroup slots (two per CU at two row tiles) each chunk gets 512 // 3 = 170, i.e.
-    42 splits of the sequence for each of the 4 KV heads; the workspace holds every row of
-    every unit."""
+    256 workgroup slots (one 8-wave workgroup per CU at two row tiles) each chunk gets
+    256 // 3 = 85, i.e. 21 splits of the sequence for each of the 4 KV heads; the workspace
+    holds every row of every unit."""
     import quantized_kv_decode_amd as qk
     d = _desc(qk, cap=10 ** 6)
     al = lambda x: (x + 255) // 256 * 256
     ws = lambda L, n_q: lib.nvfp4_decode_attn_workspace_bytes(ctypes.byref(d), 1, qk._i64([L]), n_q, 24)
-    units = 4 * ((2 * 256 // 3) // 4)
-    assert units == 168
+    units = 4 * ((256 // 3) // 4)
+    assert units == 84
     for n_q in (16, 12):
         R = 6 * n_q
-        assert ws(10 ** 6, n_q) == al(units * R * 256 * 4) + 2 * al(units * R * 4)
+        assert ws(400000, n_q) == al(units * R * 256 * 4) + 2 * al(units * R * 4)
 
 
 def test_prefill_rows_plan_fewer_units(lib):
     """Row chunks run side by side (grid y), so the planner makes proportionally fewer
-    units: 1024 query tokens at G = 6 are 6144 rows = 192 chunks of 32, and 512 / 192 = 2
-    unit slots fall below one unit per (sequence, KV head): 4 units."""
+    units: 1024 query tokens at G = 6 are 6144 rows = 192 chunks of 32, and 256 / 192 = 1
+    unit slot falls below one unit per (sequence, KV head): 4 units."""
     import quantized_kv_decode_amd as qk
     d = _desc(qk, cap=10 ** 6)
     al = lambda x: (x + 255) // 256 * 256

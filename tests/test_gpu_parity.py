@@ -13,7 +13,8 @@ import torch
 
 import oracle
 import workloads
-from helpers import TOL_REL, OracleRun, _bf16_u16, adversarial_rows, assert_planes_equal, gpu_run, max_err
+from helpers import (TOL_REL, OracleRun, _bf16_u16, adversarial_rows, assert_planes_equal, assert_same_output,
+                     deterministic, gpu_run, max_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -137,9 +138,14 @@ def test_decode_matches_oracle(qk, shape):
     pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
     assert_planes_equal(pool, ref.cache)
     _check_decode(w, ref, out)
-    # bf16 output is the round-to-nearest-even of the fp32 result
+    # bf16 output is the round-to-nearest-even of the fp32 result (of the same partition: bit
+    # for bit where the kernels are deterministic, else one bf16 step at most)
     outb = qk.decode_attn(pool, g, ref.q.cuda(), w.seq_base, list(w.seq_lens), w.sm_scale, out_dtype=torch.bfloat16)
-    assert torch.equal(outb, out.to(torch.bfloat16))
+    if deterministic(w):
+        assert torch.equal(outb, out.to(torch.bfloat16))
+    else:
+        o32 = out.float()
+        assert ((outb.float() - o32).abs() <= o32.abs() * 2.0 ** -8 + TOL_REL * ref.vmax()).all()
 
 
 STEP_SHAPES = DECODE_SHAPES + [
@@ -175,7 +181,7 @@ def test_decode_step_equals_append_then_decode(qk, shape):
     torch.cuda.synchronize()
     for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
         assert torch.equal(getattr(pool_a, name), getattr(pool_b, name)), name
-    assert torch.equal(out_a, out_b)
+    assert_same_output(out_a, out_b, w, ref.vmax())
     assert_planes_equal(pool_b, ref.cache)
     _check_decode(w, ref, out_b)
 
@@ -303,7 +309,7 @@ def test_decode_step_device_lengths_graph_replay(qk, n_q):
     first = out_buf.clone()
     graph.replay()
     torch.cuda.synchronize()
-    assert torch.equal(first, out_buf)
+    assert_same_output(first, out_buf, w, ref.vmax())
 
 
 def test_decode_deterministic_and_partial_combine_split(qk):
@@ -321,6 +327,28 @@ def test_decode_deterministic_and_partial_combine_split(qk):
     torch.cuda.synchronize()
     assert torch.equal(out, out3)
     _check_decode(w, ref, out)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(seq_lens=(9000, 3000), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=2),   # 12 rows: one tile
+    dict(seq_lens=(9000, 3000), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=4),   # 24 rows: claimed blocks
+    dict(seq_lens=(9000, 3000), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=6),   # 36 rows: pair kernel
+])
+def test_repeat_runs(qk, shape):
+    """Five runs of one step: bit-identical for one row tile and the pair kernel (fixed block
+    partitions); at two row tiles, where waves claim blocks as they free up, every run within
+    the attention tolerance of the others and of the oracle."""
+    w = workloads.small(**shape)
+    say("repeat runs", shape)
+    ref = OracleRun(w)
+    pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
+    q = ref.q.cuda()
+    outs = [out] + [qk.decode_attn(pool, g, q, w.seq_base, list(w.seq_lens), w.sm_scale) for _ in range(4)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert_same_output(outs[0], o, w, ref.vmax())
+    for o in outs:
+        _check_decode(w, ref, o)
 
 
 def test_split_plan_invariance(qk):

@@ -1,8 +1,9 @@
 """nvfp4_decode_step_noalloc: the decode step with its partials in the library's static
 per-GPU scratch array, for callers that cannot allocate. Checked through the C ABI against
 nvfp4_decode_step (the entry point it varies) on two calls in a row, the second with a
-smaller input: identical pool bytes and output bits, and both within the attention
-tolerance of the oracle."""
+smaller input: identical pool bytes, the same output (bit for bit where the kernels'
+block partition is fixed, to the attention tolerance where waves claim blocks), and both
+within the attention tolerance of the oracle."""
 import ctypes
 
 import numpy as np
@@ -10,7 +11,7 @@ import pytest
 import torch
 
 import workloads
-from helpers import TOL_REL, OracleRun, assert_planes_equal, max_err
+from helpers import TOL_REL, OracleRun, assert_planes_equal, assert_same_output, max_err
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +58,7 @@ def test_noalloc_step_matches_decode_step_twice(qk):
         torch.cuda.synchronize()
         for name in ("k_codes", "k_scales", "v_codes", "v_scales"):
             assert torch.equal(getattr(pool_a, name), getattr(pool_b, name)), name
-        assert torch.equal(out_a, out_b)
+        assert_same_output(out_a, out_b, w, ref.vmax())
         assert_planes_equal(pool_b, ref.cache)
         exp = ref.attention()
         err, tol = max_err(out_b.cpu().numpy(), exp), TOL_REL * ref.vmax()
