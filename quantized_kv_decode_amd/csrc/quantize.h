@@ -159,12 +159,41 @@ __device__ inline float fp8_row_scale(uint32_t amax_bits) {
     return (float)((double)__builtin_bit_cast(float, amax_bits << 16) / 448.0);
 }
 
+// Nearest E4M3 code to the real a / s in fp32 (a >= 0 a bf16 value, s >= 2^-60): the same
+// candidate-and-one-midpoint-test decision as e4m3_nearest, with the test taken from the sign
+// of fma(mid, s, -a). That sign is exact: fma rounds the exact mid s - a once, rounding (and
+// overflow to infinity) keeps the sign, and a nonzero difference never rounds to zero. When a
+// lies within a factor two of mid s >= 2^-70, both are multiples of 2^-93 (mid of 2^-10, s of
+// 2^-83, a >= 2^-71 of 2^-78), far above fp32's smallest normal; otherwise the difference
+// exceeds 2^-71 in size.
+__device__ inline int e4m3_nearest_f32(float a, float s, float rcp_s) {
+    const float q = fminf(a * rcp_s, 448.0f);
+    const int c = q < 0.015625f ? (int)(q * 512.0f) : (int)(f32_bits(q) >> 20) - 960;
+    const float mid = ldexpf((float)(2 * e4m3_sig(c) + 1), e4m3_ex(c) - 11);
+    const float d = fmaf(mid, s, -a);
+    const int up = d < 0.0f || (d == 0.0f && (c & 1));
+    return min(c + up, 0x7E);
+}
+
 // 16 elements of a row with row scale s -> 16 code bytes (element e in byte e of out).
+// Rows with s >= 2^-60 (amax above 448 * 2^-60, every row that is not nearly zero) take the
+// fp32 decision; smaller ones the fp64 one (both exact).
 __device__ inline void fp8_row_codes(const uint32_t (&w)[8], float s, uint32_t (&out)[4]) {
-    const double sd = (double)s;
-    const double rs = __builtin_amdgcn_rcp(sd);
 #pragma unroll
     for (int k = 0; k < 4; ++k) out[k] = 0u;
+    if (s >= 0x1p-60f) {
+        const float rs = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const float a = __builtin_bit_cast(float, (h & 0x7FFFu) << 16);
+            const int c = e4m3_nearest_f32(a, s, rs);
+            out[e >> 2] |= ((uint32_t)c | ((h >> 8) & 0x80u)) << (8 * (e & 3));
+        }
+        return;
+    }
+    const double sd = (double)s;
+    const double rs = __builtin_amdgcn_rcp(sd);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;

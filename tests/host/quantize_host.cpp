@@ -18,10 +18,12 @@ static inline uint32_t host_perm(uint32_t s0, uint32_t s1, uint32_t sel) {
 }
 static double rcp_eps = 0.0;
 static inline double host_rcp(double x) { return (1.0 / x) * (1.0 + rcp_eps); }
+static inline float host_rcpf(float x) { return (float)((1.0 / (double)x) * (1.0 + rcp_eps)); }
 static inline int min(int a, int b) { return a < b ? a : b; }
 static inline uint32_t max(uint32_t a, uint32_t b) { return a > b ? a : b; }
 #define __builtin_amdgcn_perm host_perm
 #define __builtin_amdgcn_rcp host_rcp
+#define __builtin_amdgcn_rcpf host_rcpf
 #include "quantize.h"
 
 // x: n_groups x 16 bf16 bit patterns; g: one global scale per group. Writes 8 code bytes and

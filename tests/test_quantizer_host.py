@@ -163,6 +163,32 @@ def test_fp8_rows_on_midpoints(host_quantizer):
     check_fp8(np.stack(rows))
 
 
+def test_fp8_rows_around_the_fp32_path_threshold(host_quantizer):
+    """Row scales just above and below 2^-60 (the fp32 and the fp64 decision paths), with
+    elements on E4M3 midpoints of their scale and one bf16 step either side."""
+    e4 = [oracle.e4m3_value(c) for c in range(127)]
+    rows = []
+    for k in (-61, -60, -59):
+        for f in (0.999, 1.0, 1.001):
+            top = np.array([448 * 2.0 ** k * f], np.float32)
+            tb = (np.frombuffer(top.tobytes(), np.uint32) >> 16)[0]
+            s = float(np.float32(float(bf16_value(tb)) / 448))
+            mids = np.array([(e4[i] + e4[i + 1]) / 2 * s for i in range(126)], np.float32)
+            mb = (np.frombuffer(mids.tobytes(), np.uint32) >> 16).astype(np.uint16)
+            vals = np.concatenate([mb, mb + 1, mb - 1]).astype(np.uint16)
+            for i in range(0, vals.size, 255):
+                row = np.zeros(256, np.uint16)
+                row[0] = tb
+                chunk = vals[i:i + 255]
+                row[1:1 + chunk.size] = chunk
+                rows.append(row)
+    check_fp8(np.stack(rows))
+
+
+def bf16_value(bits):
+    return np.frombuffer((np.uint32(bits) << np.uint32(16)).tobytes(), np.float32)[0]
+
+
 def test_fp8_rows_random_and_edge(host_quantizer):
     rng = np.random.default_rng(17)
     x = (rng.standard_normal((500, 256)) * 10.0 ** rng.uniform(-30, 30, (500, 1))).astype(np.float32)
