@@ -410,7 +410,7 @@ def main() -> int:
     step_gbps = kv / (ms_step * 1e-3) / 1e9
     res["achievable"] = {"GBps": round(achievable, 1), "step_frac": round(step_gbps / achievable, 4),
                          "partial_frac": round(achieved / achievable, 4),
-                         "probe": "plain streaming read of 1 GiB, 16-byte loads (nvfp4_hbm_read_probe), best of "
+                         "probe": "plain streaming read of 1 GiB, 16-byte non-temporal loads (nvfp4_hbm_read_probe), best of "
                                   "these workgroup counts", "by_workgroups": probe_rates}
     res["device_lengths_step_us"] = round(ms_dl * 1e3, 3) if dev_len else None
     res["step_us_spread"] = spread

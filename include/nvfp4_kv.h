@@ -245,7 +245,8 @@ int nvfp4_decode_attn_combine(const nvfp4_kv_cache *cache, const float *global_s
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Streaming-read probe (measurement only, not part of the decode path): reads `bytes` of
- * device memory at `buf` once with 16-byte loads from `workgroups` 256-thread workgroups and
+ * device memory at `buf` once with 16-byte non-temporal loads (the policy of the decode
+ * kernels' KV loads) from `workgroups` 256-thread workgroups and
  * writes one fold of the data per workgroup to sink[0 .. workgroups). Timing it gives the
  * read rate a plain streaming kernel reaches, the practical ceiling for the decode kernels
  * (knoopx/ninfer page, "Quick start": the engine ships a standalone HBM probe).

@@ -3,7 +3,9 @@
 // page, "Quick start": the engine ships a standalone HBM probe next to its build).
 //
 // Each thread reads 16-byte words in a grid-stride loop, four independent loads in flight
-// per trip, and folds them into one word; each workgroup writes one word of the sink, so
+// per trip, with the streaming (non-temporal) cache policy that the decode kernels' KV loads
+// use (on MI355X it reads about 11% faster than the default policy), and folds them into one
+// word; each workgroup writes one word of the sink, so
 // the reads cannot be dropped and the writes are negligible.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint8_t
                 const uint64_t j = i + k * stride;
                 // j < n keeps the offset below 2^31; past n the load is answered with zeros
                 const uint32_t off = j < n ? (uint32_t)(j * 16) : 0x80000000u;
-                v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);   // nt
             }
 #pragma unroll
             for (int k = 0; k < kUnroll; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
