@@ -25,10 +25,14 @@
 //                   scale group (a half group: D/64 code bytes per token).
 // Dequantisation work per token is that of the single-tile kernel; the accumulators
 // per wave are halved. A workgroup holds kPairs = 4 pairs (every pair a CU keeps resident)
-// that take the unit's blocks in turn and merge at the end. Every wave runs the same number of block
-// iterations (a pair with no block left runs a fully masked one on zero data), and the
-// choice of a reference update is read by every wave from the same LDS bytes, so the
-// workgroup barriers always match.
+// that merge at the end. The two waves of a pair meet through a handshake in LDS (each
+// raises its own count once its LDS writes are complete, then waits for its partner's), not
+// through workgroup barriers, so a pair never waits for the other pairs. Each pair starts
+// with blocks pair and pair + kPairs and then claims the unit's next unclaimed block from a
+// counter in LDS, one block ahead of its loads, so pairs that run faster take more blocks
+// (the partition, and with it the fp16 rounding reference of each pair, depends on timing:
+// results agree to rounding, not bit for bit). Both waves of a pair read the same claims and
+// the same reference-update flags, so they always make the same number of handshakes.
 #include "decode_common.h"
 
 namespace nvfp4 {
@@ -36,10 +40,19 @@ namespace {
 
 using namespace dev;
 
+// LDS words that the partner wave writes while this wave polls them (volatile, and typed
+// as LDS so the accesses stay LDS instructions)
+typedef volatile __attribute__((address_space(3))) uint32_t lds_vu32;
+typedef volatile __attribute__((address_space(3))) uint16_t lds_vu16;
+
+// Polls of a partner's handshake count before a wave gives up waiting. The partner always
+// arrives (both waves make the same handshakes, and every wait follows this wave's own
+// count), so the bound only keeps a mistake from hanging the device.
+constexpr int kHandshakePolls = 1 << 22;
 
 // The reference m of a row moves only when a score passes m + kPairLazy (base 2), so fp16
 // probabilities stay below 2^15 (finite: the fp16 maximum is about 2^16) and a unit's reference
-// settles after its first blocks: every later move costs the whole workgroup an exchange.
+// settles after its first blocks: every later move costs the pair an exchange.
 constexpr float kPairLazy = 15.0f;
 
 // KF: the K format (0 NVFP4; 1 the row-scaled FP8 E4M3 K of K8V4), see KGeom.
@@ -148,7 +161,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(128 * decode_pairs_per_wg(
                           amdgpu_waves_per_eu(decode_waves_per_simd(NT))))
 void decode_pair_kernel(DecodeParams p) {
     constexpr int kPairs = decode_pairs_per_wg(NT);               // wave pairs per workgroup
-    constexpr uint32_t kPairStep = kBlockTokens * kPairs;         // tokens between a pair's blocks
     constexpr int KK = D / 32;
     constexpr int HT = D / 32;          // PV output tiles per wave (half of D/16)
     constexpr int EPL = D / 16;
@@ -157,6 +169,9 @@ void decode_pair_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) u32x4_t pbuf[kPairs][2][NT][64];   // [pair][parity]: fp16 P per lane
     __shared__ float xmax[kPairs][2][NT * 16];                            // [pair][half]
     __shared__ __attribute__((aligned(8))) uint8_t mflag[2][8];           // [parity][wave]
+    __shared__ uint32_t ready[2 * kPairs];                                // per wave: handshakes made
+    __shared__ uint32_t next_blk;                                         // the unit's next unclaimed block
+    __shared__ int claim_buf[kPairs][2];                                  // [pair][parity]: claimed block
     __shared__ float sm_c[kMaxRows];
     __shared__ float sm_m[kPairs][kMaxRows];
     __shared__ float sm_l[kPairs][kMaxRows];
@@ -207,8 +222,24 @@ void decode_pair_kernel(DecodeParams p) {
         pair_load_v<D, KF>(r, vc, vs, o0);
     }
     if (wave < NT) q_store<D, KF>(p, rw, b, kh, wave, lane, qw, qlds, sm_c);
-    if (threadIdx.x < 16) (&mflag[0][0])[threadIdx.x] = 0;   // bytes of absent waves stay 0
+    if (threadIdx.x < 16) (&mflag[0][0])[threadIdx.x] = 0;
+    if (threadIdx.x < 2 * kPairs) ready[threadIdx.x] = 0;
+    if (threadIdx.x == 0) next_blk = 2 * kPairs;
     __syncthreads();
+    // Pair handshake: once this wave's LDS accesses are complete it raises its count, then
+    // waits for its partner's count to reach the same value.
+    uint32_t hs = 0;
+    auto pair_sync = [&]() __attribute__((always_inline)) {
+        hs += 1;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0) *(lds_vu32 *)&ready[wave] = hs;
+        for (int it = 0; it < kHandshakePolls; ++it) {
+            const uint32_t o = __builtin_amdgcn_readfirstlane(*(lds_vu32 *)&ready[wave ^ 1]);
+            if (o >= hs) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    };
     float cexp[NT];
     int qi[NT];
 #pragma unroll
@@ -244,22 +275,24 @@ void decode_pair_kernel(DecodeParams p) {
     }
     const half8_t ones = __builtin_bit_cast(half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
 
-    // The pair's j-th block is block pair + kPairs j of the unit. Probabilities are written
+    // The pair's blocks: pair, pair + kPairs, then the blocks it claims. Probabilities are written
     // speculatively: right after its scores, each wave turns block j's scores into fp16
     // P = 2^(x - m) with the reference m it holds, stores them (LDS, parity j & 1) and
     // raises its byte in mflag[j & 1] if any score lies above m + kPairLazy. After the
-    // barrier every wave reads all the bytes, so the decision is the workgroup's:
+    // handshake both waves read both bytes, so the decision is the pair's:
     //   none raised (the common case once the first block has set m): P(j) in LDS is final
     //     and O += P(j) . V(j) follows at once -- no row maximum is reduced or exchanged;
-    //   some raised: every pair reduces its rows' maxima of block j, exchanges them through
-    //     LDS (barrier), moves m where it is exceeded by more than kPairLazy, rescales O and
-    //     l, rewrites P(j) (barrier) -- exactly the update a per-block exchange would make,
+    //   some raised: the pair reduces its rows' maxima of block j, exchanges them through
+    //     LDS (handshake), moves m where it is exceeded by more than kPairLazy, rescales O and
+    //     l, rewrites P(j) (handshake) -- exactly the update a per-block exchange would make,
     //     so the result does not depend on which path ran.
-    // One loop trip: barrier -> [update] -> O += P(j) . V(j); V(j + 1) interleave, V(j + 2)
-    // loads; S^T(j + 1), K(j + 2) loads, P(j + 1) and its flag.
+    // One loop trip: handshake -> [update] -> O += P(j) . V(j); V(j + 1) interleave, V(j + 2)
+    // loads; S^T(j + 1), K(j + 2) loads, P(j + 1) and its flag, the claim of block j + 3.
+    // Double buffers (P, flags, claims by parity of j) are safe: a wave rewrites parity j & 1
+    // only after the handshake of trip j + 1, which its partner reaches after its last read
+    // of that parity in trip j.
     // lim: offset limit of the block relative to L - n_q (32-bit: tokens < 2^31).
-    const int lim0 = (int)(un.L - p.n_q - un.t0) - kBlockTokens * pair;
-    const int iters = max((nblk + kPairs - 1) / kPairs, 1);   // an empty unit runs one masked trip
+    const int lim0 = (int)(un.L - p.n_q - un.t0);
     // Raw MFMA scores of this wave's 16 tokens (masked: -inf). The score factor c is
     // positive (q_store), so the lane's maximum scaled score is c times max4(x).
     float x[NT][4];
@@ -281,10 +314,10 @@ void decode_pair_kernel(DecodeParams p) {
         }
     };
 
-    // S^T of the pair's block j from the K words in r, the K loads of block j + 1, the
-    // block's masked scores, its speculative probabilities and this wave's flag. A block
-    // past the pair's last one masks everything (its words are zeros).
-    auto start_block = [&](int j) __attribute__((always_inline)) {
+    // S^T of the pair's block j (unit block bj) from the K words in r, the K loads of the
+    // next block (bnext), the claim of block j + 2 (wave 0 of the pair), the block's masked
+    // scores, its speculative probabilities and this wave's flag.
+    auto start_block = [&](int j, int bj, int bnext) __attribute__((always_inline)) {
         asm volatile("" ::: "memory");     // Q fragments are re-read from LDS every block
         float4_t s[NT];
 #pragma unroll
@@ -305,8 +338,9 @@ void decode_pair_kernel(DecodeParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) s[rt][i] *= __builtin_bit_cast(float, r.ks[i]);
         }
-        pair_load_k<D, KF>(r, kc, ks, offs_for(pair + kPairs * (j + 1)));
-        const int lim = pair + kPairs * j < nblk ? lim0 - (int)kPairStep * j : -(1 << 30);
+        pair_load_k<D, KF>(r, kc, ks, offs_for(bnext));
+        if (w == 0 && lane == 0) claim_buf[pair][j & 1] = (int)atomicAdd(&next_blk, 1u);
+        const int lim = lim0 - kBlockTokens * bj;
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
@@ -326,7 +360,7 @@ void decode_pair_kernel(DecodeParams p) {
         if (lane == 0) mflag[j & 1][wave] = flag;
     };
 
-    // The reference update for block j (every wave of the workgroup, see above).
+    // The reference update for block j (both waves of the pair, see above).
     auto update = [&](int j) __attribute__((always_inline)) {
         float mloc[NT];
 #pragma unroll
@@ -334,7 +368,7 @@ void decode_pair_kernel(DecodeParams p) {
             mloc[rt] = wave_max_g(max4(x[rt]) * cexp[rt]);
             if (g == 0) xmax[pair][w][16 * rt + n] = mloc[rt];
         }
-        __syncthreads();
+        pair_sync();
         bool need_any = false;
         float alpha[NT];
 #pragma unroll
@@ -361,7 +395,7 @@ void decode_pair_kernel(DecodeParams p) {
             }
         }
         write_p(j);
-        __syncthreads();
+        pair_sync();
     };
 
     // O += P(j) . V(j) over this wave's half of head_dim, P(j) of both waves from LDS.
@@ -398,28 +432,34 @@ void decode_pair_kernel(DecodeParams p) {
     };
 
     PairVPrep vprep;
-    auto trip = [&](int j, bool do_next) __attribute__((always_inline)) {
-        __syncthreads();                   // P(j) and the flags of every wave
-        const uint32_t f0 = __builtin_amdgcn_readfirstlane(reinterpret_cast<const volatile uint32_t *>(mflag[j & 1])[0]);
-        const uint32_t f1 = __builtin_amdgcn_readfirstlane(reinterpret_cast<const volatile uint32_t *>(mflag[j & 1])[1]);
+    int bj = pair, bj1 = pair + kPairs;    // this pair's blocks j and j + 1
+    auto trip = [&](int j) __attribute__((always_inline)) {
+        pair_sync();                       // P(j), the flags and the claim of both waves
+        const int bj2 = __builtin_amdgcn_readfirstlane((int)*(lds_vu32 *)&claim_buf[pair][j & 1]);
+        const uint32_t flags = __builtin_amdgcn_readfirstlane((uint32_t)*((lds_vu16 *)&mflag[j & 1][0] + pair));
         half8_t pa[NT];
         read_p(j, pa);                     // final unless the update below rewrites P(j)
-        if ((f0 | f1) != 0) {
+        if (flags != 0) {
             update(j);
             read_p(j, pa);
         }
         pv_block(pa, vprep);
         pair_v_prep<D, KF>(vprep, r);
         __builtin_amdgcn_sched_barrier(0);
-        pair_load_v<D, KF>(r, vc, vs, offs_for(pair + kPairs * (j + 2)));
-        if (do_next) start_block(j + 1);
+        pair_load_v<D, KF>(r, vc, vs, offs_for(bj2));
+        if (bj1 < nblk) start_block(j + 1, bj1, bj2);
+        bj = bj1;
+        bj1 = bj2;
     };
 
-    start_block(0);
-    pair_v_prep<D, KF>(vprep, r);
-    pair_load_v<D, KF>(r, vc, vs, offs_for(pair + kPairs));
-    for (int j = 0; j < iters - 1; ++j) trip(j, true);
-    trip(iters - 1, false);
+    // A pair's blocks increase (its first two are below every claim), so it is done at its
+    // first block past the unit's end.
+    if (bj < nblk) {
+        start_block(0, bj, bj1);
+        pair_v_prep<D, KF>(vprep, r);
+        pair_load_v<D, KF>(r, vc, vs, offs_for(bj1));
+        for (int j = 0; bj < nblk; ++j) trip(j);
+    }
 
     // ---- merge the two pairs and write the unit's partial
 #pragma unroll

@@ -312,20 +312,24 @@ def test_decode_step_device_lengths_graph_replay(qk, n_q):
     assert_same_output(first, out_buf, w, ref.vmax())
 
 
-def test_decode_deterministic_and_partial_combine_split(qk):
-    w = workloads.small(seq_lens=(5000, 1234), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=6)
-    say("determinism")
+@pytest.mark.parametrize("n_q", [2, 6])      # 12 rows: one row tile; 36 rows: the pair kernel
+def test_decode_deterministic_and_partial_combine_split(qk, n_q):
+    """A second run, and the step as separate partial and combine calls, give the same output:
+    bit for bit at one row tile (a fixed block partition), within the attention tolerance in
+    the pair kernel (pairs claim blocks as they free up)."""
+    w = workloads.small(seq_lens=(5000, 1234), num_kv_heads=4, num_q_heads=24, head_dim=256, n_q=n_q)
+    say("determinism", n_q)
     ref = OracleRun(w)
     pool, g, out = gpu_run(w, ref.k, ref.v, ref.q)
     q = ref.q.cuda()
     out2 = qk.decode_attn(pool, g, q, w.seq_base, list(w.seq_lens), w.sm_scale)
-    assert torch.equal(out, out2)
+    assert_same_output(out, out2, w, ref.vmax())
     ws = qk.alloc_workspace(pool, list(w.seq_lens), w.n_q, w.num_q_heads)
     out3 = torch.empty_like(out)
     qk.decode_attn_partial(pool, g, q, w.seq_base, list(w.seq_lens), w.sm_scale, ws)
     qk.decode_attn_combine(pool, g, out3, list(w.seq_lens), ws)
     torch.cuda.synchronize()
-    assert torch.equal(out, out3)
+    assert_same_output(out, out3, w, ref.vmax())
     _check_decode(w, ref, out)
 
 
@@ -335,9 +339,9 @@ def test_decode_deterministic_and_partial_combine_split(qk):
     dict(seq_lens=(9000, 3000), num_kv_heads=2, num_q_heads=12, head_dim=256, n_q=6),   # 36 rows: pair kernel
 ])
 def test_repeat_runs(qk, shape):
-    """Five runs of one step: bit-identical for one row tile and the pair kernel (fixed block
-    partitions); at two row tiles, where waves claim blocks as they free up, every run within
-    the attention tolerance of the others and of the oracle."""
+    """Five runs of one step: bit-identical for one row tile (a fixed block partition); at two
+    row tiles and in the pair kernel, where waves or pairs claim blocks as they free up, every
+    run within the attention tolerance of the others and of the oracle."""
     w = workloads.small(**shape)
     say("repeat runs", shape)
     ref = OracleRun(w)
