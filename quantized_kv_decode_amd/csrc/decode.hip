@@ -314,12 +314,11 @@ __device__ inline void pv_block(State<D, NT> &st, const VPrep<D> &vp, const half
         st.lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rt], ones, st.lsum[rt], 0, 0, 0);
 }
 
-template <int D, int NT>
+template <int D, int NT, int W>
 struct Lds {
     static constexpr int KK = D / 32;
-    static constexpr int STRIDE = D + 4;                       // merge rows, padded
     static constexpr int Q_BYTES = NT * KK * 64 * 16;          // Q fragments [NT][KK][lane]
-    static constexpr int MERGE_BYTES = kWaves * 16 * STRIDE * 4;
+    static constexpr int MERGE_BYTES = W * (D / 16) * 64 * 16; // one row tile of every wave
     static constexpr int BYTES = Q_BYTES > MERGE_BYTES ? Q_BYTES : MERGE_BYTES;
 };
 
@@ -330,7 +329,7 @@ void decode_partial_kernel(DecodeParams p) {
     constexpr int EPL = D / 16;
     constexpr int W = decode_partial_waves(NT);
     constexpr bool kClaim = NT == 2;       // waves claim blocks (else a fixed stride of W)
-    using LD = Lds<D, NT>;
+    using LD = Lds<D, NT, W>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LD::BYTES];
     __shared__ float sm_c[kMaxRows];
     __shared__ float sm_m[W][kMaxRows];
@@ -453,13 +452,15 @@ void decode_partial_kernel(DecodeParams p) {
         kb = kn;
     }
 
-    // ---- merge the four waves' (o, m, l) and write the unit's partial
+    // ---- merge the waves' (o, m, l) and write the unit's partial
+    // Lane indices are recomputed here rather than held in registers across the block loop.
+    const int mlane = __lane_id(), mg = mlane >> 4, mn = mlane & 15;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-        if (g == 0) sm_m[wave][16 * rt + n] = st.m[rt];          // m: row 16 rt + n
-        if (n == 0) {                                             // l: rows 16 rt + 4 g + i
+        if (mg == 0) sm_m[wave][16 * rt + mn] = st.m[rt];        // m: row 16 rt + n
+        if (mn == 0) {                                            // l: rows 16 rt + 4 g + i
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm_l[wave][16 * rt + 4 * g + i] = st.lsum[rt][i];
+            for (int i = 0; i < 4; ++i) sm_l[wave][16 * rt + 4 * mg + i] = st.lsum[rt][i];
         }
     }
     __syncthreads();                                  // also ends every read of the Q fragments
@@ -467,7 +468,7 @@ void decode_partial_kernel(DecodeParams p) {
     for (int rt = 0; rt < NT; ++rt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * rt + 4 * g + i;
+            const int row = 16 * rt + 4 * mg + i;
             float M = -INFINITY;
 #pragma unroll
             for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][row]);
@@ -477,69 +478,36 @@ void decode_partial_kernel(DecodeParams p) {
             for (int dt = 0; dt < EPL; ++dt) st.acc[rt][dt][i] *= f;
         }
     }
-    float(*buf)[16][LD::STRIDE] = reinterpret_cast<float(*)[16][LD::STRIDE]>(lds);
+    // Sum of the W waves' accumulators, one row tile at a time. Each wave stores its tile
+    // as EPL float4 rows of 64 lanes (1 KB, lane-contiguous: conflict-free stores), lane L of
+    // row dt at slot L ^ dt. A thread then sums the W copies of one (dt, L) float4 -- lanes
+    // dt = 0..15 of a 16-lane group read slots L ^ dt, all in different banks -- and
+    // stores its 4 rows; for each row a wave's stores cover 64 consecutive floats.
+    u32x4_t *mrg = reinterpret_cast<u32x4_t *>(lds);
     float *ws_o = p.ws_o + ((int64_t)u * Rt + row0) * D;
+    constexpr int UNITS = EPL * 64;                   // (dt, lane) float4s per wave and tile
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-        if constexpr (W == 8) {
-            // waves 4..7 hand their rows to waves 0..3 through the merge buffer first
-            if (wave >= 4) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float *dst = &buf[wave - 4][4 * g + i][EPL * n];
-#pragma unroll
-                    for (int dt = 0; dt < EPL; dt += 4)
-                        *reinterpret_cast<float4_t *>(dst + dt) = float4_t{st.acc[rt][dt][i], st.acc[rt][dt + 1][i],
-                                                                           st.acc[rt][dt + 2][i], st.acc[rt][dt + 3][i]};
-                }
-            }
-            __syncthreads();
-            if (wave < 4) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float *src = &buf[wave][4 * g + i][EPL * n];
-#pragma unroll
-                    for (int dt = 0; dt < EPL; dt += 4) {
-                        const float4_t v = *reinterpret_cast<const float4_t *>(src + dt);
-                        st.acc[rt][dt][i] += v[0]; st.acc[rt][dt + 1][i] += v[1];
-                        st.acc[rt][dt + 2][i] += v[2]; st.acc[rt][dt + 3][i] += v[3];
-                    }
-                }
-            }
-            __syncthreads();
-        }
-        // Only rows below R are stored. Lane n's D/16 values sit at a stride of D/16 floats
-        // from lane n + 1's, so lanes n, n + 2, ... share LDS banks; rotating the order of the
-        // 4-float chunks by n / 2 spreads them over the banks.
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (wave < 4 && 16 * rt + 4 * g + i < R) {
-                float *dst = &buf[wave][4 * g + i][EPL * n];
-#pragma unroll
-                for (int c = 0; c < EPL / 4; ++c) {
-                    const int dt = 4 * ((c + (n >> 1)) & (EPL / 4 - 1));
-                    float4_t v;
-#pragma unroll
-                    for (int k = 0; k < EPL / 4; ++k)      // select chunk dt without dynamic indexing
-                        if (4 * k == dt) v = float4_t{st.acc[rt][4 * k][i], st.acc[rt][4 * k + 1][i],
-                                                      st.acc[rt][4 * k + 2][i], st.acc[rt][4 * k + 3][i]};
-                    *reinterpret_cast<float4_t *>(dst + dt) = v;
-                }
-            }
-        }
+        for (int dt = 0; dt < EPL; ++dt)
+            mrg[(wave * EPL + dt) * 64 + (mlane ^ dt)] = __builtin_bit_cast(u32x4_t, st.acc[rt][dt]);
         __syncthreads();
-        const int rows = min(16, R - 16 * rt);
-        for (int e = threadIdx.x; e < rows * D; e += 64 * W) {
-            const int r16 = e / D, d = e - r16 * D;
-            float sum = 0.f;
+        for (int e = wave * 64 + mlane; e < UNITS; e += 64 * W) {
+            const int dt = e % EPL, L = e / EPL;          // L = 16 g' + n'
+            float4_t s = __builtin_bit_cast(float4_t, mrg[dt * 64 + (L ^ dt)]);
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) sum += buf[w][r16][d];
-            ws_o[(int64_t)(16 * rt + r16) * D + d] = sum;
+            for (int w = 1; w < W; ++w) s += __builtin_bit_cast(float4_t, mrg[(w * EPL + dt) * 64 + (L ^ dt)]);
+            const int gg = L >> 4, nn = L & 15;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * rt + 4 * gg + i;
+                if (row < R) ws_o[(int64_t)row * D + EPL * nn + dt] = s[i];
+            }
         }
         __syncthreads();
     }
-    if ((int)threadIdx.x < R) {
-        const int row = threadIdx.x;
+    if (wave * 64 + mlane < R) {
+        const int row = wave * 64 + mlane;
         float M = -INFINITY;
         for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][row]);
         float Ls = 0.f;
