@@ -94,18 +94,18 @@ __device__ inline void load_k(Raw<D, KF> &r, rsrc_t kc, rsrc_t ks, const Offs &o
         if (PART == 0 || PART == mt + 1) {
 #pragma unroll
             for (int c = 0; c < Raw<D, KF>::KW / 4; ++c) {
-                const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, oc + 16 * c, 0, kStreamLoad);
+                const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, oc + 16 * c, 0, kKLoadPolicy<KF>);
                 r.k[mt][4 * c] = a[0]; r.k[mt][4 * c + 1] = a[1]; r.k[mt][4 * c + 2] = a[2]; r.k[mt][4 * c + 3] = a[3];
             }
         }
         if (PART == 1) continue;
         if constexpr (KF == 1) {
-            const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(ks, os, 0, kStreamLoad);
+            const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(ks, os, 0, kKLoadPolicy<KF>);
             r.ks[mt][0] = b[0]; r.ks[mt][1] = b[1]; r.ks[mt][2] = b[2]; r.ks[mt][3] = b[3];
         } else if constexpr (D == 256) {
-            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b32(ks, os, 0, kStreamLoad);
+            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b32(ks, os, 0, kKLoadPolicy<KF>);
         } else {
-            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b16(ks, os, 0, kStreamLoad);
+            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b16(ks, os, 0, kKLoadPolicy<KF>);
         }
     }
 }

@@ -78,6 +78,11 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // once per step, so keeping it is of no use; with the streaming policy a plain 16-byte read
 // sweep of 1 GiB on MI355X went from 6.38 to 7.07 TB/s (and the decode steps 2-6% faster).
 constexpr int kStreamLoad = 2;
+// The FP8 K planes of K8V4 keep the default policy (same box, A/B in one process: with
+// streaming K loads the 330k-470k-token K8V4 decode took 443 us per step, with default-policy
+// K loads and streaming V loads 327 us; the NVFP4 K loads gain from streaming).
+template <int KF>
+constexpr int kKLoadPolicy = KF ? 0 : kStreamLoad;
 
 // Raw buffer over one head plane: loads past its end return zeros (no fault).
 __device__ inline rsrc_t plane_rsrc(const uint8_t *base, uint32_t bytes) {
