@@ -94,18 +94,18 @@ __device__ inline void load_k(Raw<D, KF> &r, rsrc_t kc, rsrc_t ks, const Offs &o
         if (PART == 0 || PART == mt + 1) {
 #pragma unroll
             for (int c = 0; c < Raw<D, KF>::KW / 4; ++c) {
-                const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, oc + 16 * c, 0, kKLoadPolicy<KF>);
+                const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, oc + 16 * c, 0, kKCodePolicy<KF>);
                 r.k[mt][4 * c] = a[0]; r.k[mt][4 * c + 1] = a[1]; r.k[mt][4 * c + 2] = a[2]; r.k[mt][4 * c + 3] = a[3];
             }
         }
         if (PART == 1) continue;
         if constexpr (KF == 1) {
-            const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(ks, os, 0, kKLoadPolicy<KF>);
+            const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(ks, os, 0, kScalePolicy);
             r.ks[mt][0] = b[0]; r.ks[mt][1] = b[1]; r.ks[mt][2] = b[2]; r.ks[mt][3] = b[3];
         } else if constexpr (D == 256) {
-            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b32(ks, os, 0, kKLoadPolicy<KF>);
+            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b32(ks, os, 0, kScalePolicy);
         } else {
-            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b16(ks, os, 0, kKLoadPolicy<KF>);
+            r.ks[mt][0] = __builtin_amdgcn_raw_buffer_load_b16(ks, os, 0, kScalePolicy);
         }
     }
 }
@@ -117,12 +117,12 @@ __device__ inline void load_v(Raw<D, KF> &r, rsrc_t vc, rsrc_t vs, const Offs &o
         const uint32_t dtok = 16 * (j >> 2) + (j & 3);
         if constexpr (D == 256) {
             typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-            const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(vc, o.vc + dtok * (D / 2), 0, kStreamLoad);
+            const u32x2_t a = __builtin_amdgcn_raw_buffer_load_b64(vc, o.vc + dtok * (D / 2), 0, kCodePolicy);
             r.v[j][0] = a[0]; r.v[j][1] = a[1];
         } else {
-            r.v[j][0] = __builtin_amdgcn_raw_buffer_load_b32(vc, o.vc + dtok * (D / 2), 0, kStreamLoad);
+            r.v[j][0] = __builtin_amdgcn_raw_buffer_load_b32(vc, o.vc + dtok * (D / 2), 0, kCodePolicy);
         }
-        r.vs[j] = __builtin_amdgcn_raw_buffer_load_b8(vs, o.vs + dtok * (D / 16), 0, kStreamLoad);
+        r.vs[j] = __builtin_amdgcn_raw_buffer_load_b8(vs, o.vs + dtok * (D / 16), 0, kScalePolicy);
     }
 }
 

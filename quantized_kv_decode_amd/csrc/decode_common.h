@@ -74,15 +74,18 @@ __device__ inline float max4(const float (&x)[4]) {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-// Cache policy of the KV plane loads: nt (non-temporal, streaming). Every KV byte is read
-// once per step, so keeping it is of no use; with the streaming policy a plain 16-byte read
-// sweep of 1 GiB on MI355X went from 6.38 to 7.07 TB/s (and the decode steps 2-6% faster).
-constexpr int kStreamLoad = 2;
-// The FP8 K planes of K8V4 keep the default policy (same box, A/B in one process: with
-// streaming K loads the 330k-470k-token K8V4 decode took 443 us per step, with default-policy
-// K loads and streaming V loads 327 us; the NVFP4 K loads gain from streaming).
+// Cache policy of the KV plane loads. Code loads (whole lines, every byte read once per
+// step) use nt, the non-temporal streaming policy: a plain 16-byte read sweep of 1 GiB on
+// MI355X went from 6.38 to 7.07 TB/s with it. Scale loads (a few bytes per lane, several
+// lanes per line) keep the default policy: same box, A/B in one process, per decode step,
+// streaming codes with default-policy scales against streaming everything: 237.9 vs 249.1 us
+// (three sessions of 330k-470k tokens), 106.1 vs 114.8 us (600k tokens), 49.8 vs 51.3 us
+// (MTP verify, 131k). The FP8 K codes of K8V4 keep the default policy too (with streaming
+// K loads that decode took 443 us per step, without 327 us).
+constexpr int kCodePolicy = 2;           // nt
+constexpr int kScalePolicy = 0;
 template <int KF>
-constexpr int kKLoadPolicy = KF ? 0 : kStreamLoad;
+constexpr int kKCodePolicy = KF ? 0 : kCodePolicy;
 
 // Raw buffer over one head plane: loads past its end return zeros (no fault).
 __device__ inline rsrc_t plane_rsrc(const uint8_t *base, uint32_t bytes) {

@@ -71,16 +71,16 @@ template <int D, int KF>
 __device__ inline void pair_load_k(PairRaw<D, KF> &r, rsrc_t kc, rsrc_t ks, const Offs &o) {
 #pragma unroll
     for (int c = 0; c < PairRaw<D, KF>::KW / 4; ++c) {
-        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, o.kc + 16 * c, 0, kKLoadPolicy<KF>);
+        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(kc, o.kc + 16 * c, 0, kKCodePolicy<KF>);
         r.k[4 * c] = a[0]; r.k[4 * c + 1] = a[1]; r.k[4 * c + 2] = a[2]; r.k[4 * c + 3] = a[3];
     }
     if constexpr (KF == 1) {
-        const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(ks, o.ks, 0, kKLoadPolicy<KF>);
+        const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(ks, o.ks, 0, kScalePolicy);
         r.ks[0] = b[0]; r.ks[1] = b[1]; r.ks[2] = b[2]; r.ks[3] = b[3];
     } else if constexpr (D == 256) {
-        r.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(ks, o.ks, 0, kKLoadPolicy<KF>);
+        r.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(ks, o.ks, 0, kScalePolicy);
     } else {
-        r.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(ks, o.ks, 0, kKLoadPolicy<KF>);
+        r.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(ks, o.ks, 0, kScalePolicy);
     }
 }
 
@@ -92,10 +92,10 @@ __device__ inline void pair_load_v(PairRaw<D, KF> &r, rsrc_t vc, rsrc_t vs, cons
     for (int j = 0; j < 8; ++j) {
         const uint32_t dtok = 16 * (j >> 2) + (j & 3);
         if constexpr (D == 256)
-            r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vc, o.vc + dtok * (D / 2), 0, kStreamLoad);
+            r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(vc, o.vc + dtok * (D / 2), 0, kCodePolicy);
         else
-            r.v[j] = __builtin_amdgcn_raw_buffer_load_b16(vc, o.vc + dtok * (D / 2), 0, kStreamLoad);
-        r.vs[j] = __builtin_amdgcn_raw_buffer_load_b8(vs, o.vs + dtok * (D / 16), 0, kStreamLoad);
+            r.v[j] = __builtin_amdgcn_raw_buffer_load_b16(vc, o.vc + dtok * (D / 2), 0, kCodePolicy);
+        r.vs[j] = __builtin_amdgcn_raw_buffer_load_b8(vs, o.vs + dtok * (D / 16), 0, kScalePolicy);
     }
 }
 
