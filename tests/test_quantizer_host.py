@@ -198,3 +198,25 @@ def test_fp8_rows_random_and_edge(host_quantizer):
     edge[2, 5] = 0x0001                                        # smallest bf16 subnormal as the max
     edge[3, 7] = 0x7F7F                                        # largest finite bf16
     check_fp8(np.concatenate([xb, edge]))
+
+
+def test_calibrated_scales_near_ties(host_quantizer):
+    """Groups and rows under scales calibrated from their own data -- g = fp32(amax / 2688), row
+    scale fp32(amax / 448), amax a bf16 value -- for every amax significand of a binade. With
+    8-bit significands, many quotients then lie within 2^-24 of an E2M1 or E4M3 midpoint (the
+    rounding of the scale decides them): the regime in which the fast path's hardware bounds
+    round apart and its exact midpoint test decides."""
+    rng = np.random.default_rng(5)
+    amax = (0x4000 + np.arange(128)).astype(np.uint16)            # 2.0 .. 3.98, every significand
+    av = np.array([bf16_value(a) for a in amax], np.float64)
+    n = 96
+    x = np.zeros((amax.size, n, 16), np.uint16)
+    for i, a in enumerate(amax):
+        v = (rng.uniform(0, 1, (n, 16)) * av[i]).astype(np.float32)
+        b = (np.frombuffer(v.tobytes(), np.uint32) >> 16).astype(np.uint16).reshape(n, 16)
+        b |= (rng.integers(0, 2, (n, 16)) << 15).astype(np.uint16)
+        b[:, 0] = a                                                # the sequence maximum in every group
+        x[i] = b
+    g = np.repeat(np.array([np.float32(v / 2688) for v in av], np.float32), n)
+    check(host_quantizer, x.reshape(-1, 16), g)
+    check_fp8(x.reshape(-1, 256))
