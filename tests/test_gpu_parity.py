@@ -75,6 +75,32 @@ def test_append_adversarial_groups(qk, gval):
     assert_planes_equal(pool, ref)
 
 
+@pytest.mark.parametrize("kv_format", ["nvfp4", "k8v4"])
+def test_append_mixed_scale_ranges_in_one_wave(qk, kv_format):
+    """Ragged sequences whose global scales alternate between the fast path's range and
+    outside it (1e-40, 2.5e30, 0: the exact decision), so that lanes of one wave (four rows of
+    one plane at head_dim 256) take different paths; planes bit-exact against the oracle."""
+    D, H = 256, 2
+    lens = [3, 5, 2, 6, 1, 7]
+    n = sum(lens)
+    rows = adversarial_rows(D)
+    reps = -(-n * H // rows.shape[0])
+    x = workloads.from_u16(np.tile(rows, (reps, 1))[:n * H]).reshape(n, H, D)
+    gvals = [1.0, 1e-40, 2.5e30, 0.37, 0.0, 3.0, 7.1e-36, 0.002]
+    g = np.array([[[gvals[(2 * b + h + kv) % len(gvals)] for kv in range(2)] for h in range(H)]
+                  for b in range(len(lens))], np.float32)
+    say("mixed-range append", kv_format, lens)
+    base = [0] + [int(v) for v in np.cumsum(lens)[:-1]]
+    ref = oracle.Cache(H, D, n, kv_format=kv_format)
+    xu = workloads.as_u16(x)
+    oracle.append(ref, xu, xu, g, base, [0] * len(lens), lens)
+    pool = qk.KVPool(H, D, n, kv_format=kv_format)
+    xd = x.cuda()
+    qk.append(pool, xd, xd, torch.from_numpy(g).cuda(), base, [0] * len(lens), lens)
+    torch.cuda.synchronize()
+    assert_planes_equal(pool, ref)
+
+
 def test_calibrate_edge_values(qk):
     D = 128
     say("calibrate edges")
