@@ -220,3 +220,35 @@ def test_calibrated_scales_near_ties(host_quantizer):
     g = np.repeat(np.array([np.float32(v / 2688) for v in av], np.float32), n)
     check(host_quantizer, x.reshape(-1, 16), g)
     check_fp8(x.reshape(-1, 256))
+
+
+def test_fast_path_range_edges(host_quantizer):
+    """Global scales at the edges of the fast path's range (2^-100 and 2^100, exactly and one
+    ulp either side) and FP8 row scales around 2^-100 (rows with amax near 448 * 2^-100) and
+    near the largest bf16: groups on either side of the switch between the hardware-conversion
+    path and the exact decision agree with the oracle."""
+    ulp = lambda v, k: np.array([np.nextafter(np.float32(v), np.float32(np.inf if k > 0 else 0))], np.float32)[0]
+    gs = []
+    for e in (-100, 100):
+        v = np.float32(2.0 ** e)
+        gs += [v, ulp(v, 1), ulp(v, -1)]
+    x = adversarial_rows(256).reshape(-1, 16)
+    rng = np.random.default_rng(9)
+    rnd = rng.integers(0, 0x7F80, (400, 16)).astype(np.uint16)
+    for gv in gs:
+        check(host_quantizer, x, np.full(x.shape[0], gv, np.float32))
+        check(host_quantizer, rnd, np.full(rnd.shape[0], gv, np.float32))
+    # FP8 rows: maxima 448 * 2^-100 and its bf16 neighbours (row scales around 2^-100), and
+    # the largest finite bf16 magnitudes
+    tops = []
+    t = np.array([448 * 2.0 ** -100], np.float32)
+    tb = int((np.frombuffer(t.tobytes(), np.uint32) >> 16)[0])
+    tops += [tb - 1, tb, tb + 1, 0x7F7F, 0x7F7E]
+    rows = np.zeros((len(tops) * 4, 128), np.uint16)
+    for i, top in enumerate(tops):
+        for r in range(4):
+            row = rng.integers(0, top + 1, 128).astype(np.uint16)
+            row[0] = top
+            row |= (rng.integers(0, 2, 128) << 15).astype(np.uint16) * (np.arange(128) > 0)
+            rows[4 * i + r] = row
+    check_fp8(rows)
