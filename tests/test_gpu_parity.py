@@ -101,6 +101,44 @@ def test_append_mixed_scale_ranges_in_one_wave(qk, kv_format):
     assert_planes_equal(pool, ref)
 
 
+@pytest.mark.parametrize("kv_format", ["nvfp4", "k8v4"])
+def test_append_graph_replay(qk, kv_format):
+    """The append kernel captured once in a HIP graph and replayed three times, with new rows
+    and new global scales copied into the same buffers between replays (eager work and a
+    synchronisation between them): after every replay the pool holds the oracle's bytes for
+    that replay's rows at slots [10, 50), and zeros elsewhere."""
+    D, H, n, cap = 256, 2, 40, 96
+    say("append graph replay", kv_format)
+    pool = qk.KVPool(H, D, cap, kv_format=kv_format)
+    k_buf = torch.zeros((n, H, D), dtype=torch.bfloat16, device="cuda")
+    v_buf = torch.zeros_like(k_buf)
+    g_buf = torch.zeros((1, H, 2), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            qk.append(pool, k_buf, v_buf, g_buf, [10], [0], [n])
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(31)
+    for rep in range(3):
+        k = (torch.randn((n, H, D), generator=gen) * (1 + 3 * rep)).to(torch.bfloat16)
+        v = (torch.randn((n, H, D), generator=gen) * 0.1 ** rep).to(torch.bfloat16)
+        ku, vu = workloads.as_u16(k), workloads.as_u16(v)
+        g = oracle.calibrate(ku, vu, [n])
+        k_buf.copy_(k)
+        v_buf.copy_(v)
+        g_buf.copy_(torch.from_numpy(g))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.Cache(H, D, cap, kv_format=kv_format)
+        oracle.append(ref, ku, vu, g, [10], [0], [n])
+        assert_planes_equal(pool, ref)
+
+
 def test_calibrate_edge_values(qk):
     D = 128
     say("calibrate edges")
