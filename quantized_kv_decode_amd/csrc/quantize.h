@@ -214,16 +214,17 @@ __device__ inline void fp8_row_codes_exact(const uint32_t (&w)[8], float s, uint
 // that code is x's own nearest code. The bounds of a quotient a / b are a * r (1 -+ 2^-19)
 // in fp32, with r = v_rcp_f32 (within one ulp) of the fp32-rounded b: the reciprocal's error
 // and the three roundings stay below 2^-22 relative, far inside the 2^-19 margin, while
-// every operand is a normal number (divisors within 2^-109..2^109; a product that underflows
-// lies far below the first midpoint, where both bounds give code 0).
+// every operand is a normal number (group divisors within 2^-109..2^109, FP8 row scales
+// within 2^-100..2^120, so every reciprocal is normal; a product that underflows lies far
+// below the first midpoint, where both bounds give code 0).
 //
 // Where the two codes differ, a midpoint m lies between the bounds (one only: midpoints are
 // far more than 2^-18 apart, so the codes are c and c + 1), and the exact code is c + [a >
 // m b] (a tie to the even one). That test is exact in fp32: m b = p + e with p = fl(m b) and
 // e = fma(m, b, -p) (m has at most seven significant bits, so the product's bits and its
-// residual are representable, subnormal residuals included, for b >= 2^-109), and a - p is
-// exact because a lies within a factor (1 +- 2^-17) of m b (Sterbenz); so a - m b has the
-// sign of (a - p) - e. Such quotients are common: with g = amax / 2688 and bf16 inputs
+// residual are representable, subnormal residuals included, for b >= 2^-109; m b stays
+// finite, being within 2^-17 of a finite input), and a - p is exact because a lies within a
+// factor (1 +- 2^-17) of m b (Sterbenz); so a - m b has the sign of (a - p) - e. Such quotients are common: with g = amax / 2688 and bf16 inputs
 // (8-bit significands), many are a midpoint times (1 + the rounding error of g). Only scales
 // outside the ranges above, or non-finite inputs, take the exact decision of the first part.
 constexpr float kBelow = 0x1.ffffcp-1f;        // 1 - 2^-19
